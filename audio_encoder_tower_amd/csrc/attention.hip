@@ -1,0 +1,287 @@
+// Bidirectional multi-head attention of the encoder blocks, head_dim 64.
+//
+// Every position attends to every valid position of its own clip: one pass,
+// no causal mask, nothing cached ("Qwen2-Audio-7B-Instruct", (1) AUDIO
+// ENCODER: single bidirectional pass; "Voxtral-Mini-3B-2507", (1) AUDIO
+// ENCODER: 20 heads and 20 KV heads, head_dim 64). Clips are packed: clip b
+// owns rows [start[b], start[b] + len[b]) and masked positions were removed
+// beforehand, so the only masking left is the ragged end of each clip.
+//
+// bf16 kernel (flash-style, one pass over the keys with an online softmax):
+//   - workgroup = (128-query tile, head, clip), four wave64s with 32 queries each;
+//   - 64-key tiles of K (row-major) and V (already transposed by the QKV
+//     GEMM's epilogue) are staged in LDS, double-buffered through registers;
+//   - S^T = K Q^T on v_mfma_f32_32x32x16_bf16, so each lane holds 32 scores of
+//     a single query (its partner lane l^32 holds the other 32): the row max
+//     and row sum need one cross-lane exchange per tile, not a tree;
+//   - P^T in registers is exactly the B operand of O^T = V^T P^T, so P never
+//     goes through LDS; V^T's keys are stored in the order that matches;
+//   - scores are scaled by 1/sqrt(64) and turned into base-2 exponents in a
+//     single fma; softmax statistics and the output accumulate in fp32.
+#include "common.h"
+#include "launch.h"
+
+namespace aenc {
+
+constexpr int ATT_BQ = 128;
+constexpr int ATT_BK = 64;
+constexpr int ATT_D = 64;
+
+__device__ __forceinline__ int att_swz(int row, int chunk) { return chunk ^ (row & 7); }
+
+__global__ __launch_bounds__(256) void attention_bf16_kernel(const bf16_t* __restrict__ qk, int64_t ld_qk,
+                                                             const bf16_t* __restrict__ vt, int64_t ld_vt,
+                                                             const int32_t* __restrict__ starts,
+                                                             const int32_t* __restrict__ lens, int d,
+                                                             bf16_t* __restrict__ o, int64_t ld_o) {
+  __shared__ __align__(16) bf16_t Ks[2][ATT_BK * ATT_D];   // [key][dim], swizzled 16-byte chunks
+  __shared__ __align__(16) bf16_t Vs[2][ATT_D * ATT_BK];   // [dim][key position], swizzled
+
+  const int b = blockIdx.z, h = blockIdx.y;
+  const int start = starts[b];
+  const int len = lens[b];
+  const int q0 = blockIdx.x * ATT_BQ;
+  if (q0 >= len) return;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int fq = lane & 31, hh = lane >> 5;
+  const int qi = q0 + wave * 32 + fq;                       // this lane's query (clip-relative)
+
+  // Q fragments (B operand of S^T = K Q^T): dims 16s + 8hh .. +7.
+  bf16x8 qf[4];
+  {
+    const bf16_t* qrow = qk + (int64_t)(start + min(qi, len - 1)) * ld_qk + h * ATT_D + 8 * hh;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qf[s] = *(const bf16x8*)(qrow + 16 * s);
+  }
+
+  // Cooperative tile loads: two 16-byte chunks of K and two of V^T per thread.
+  const bf16_t* kbase = qk + d + h * ATT_D;
+  const bf16_t* vbase = vt + (int64_t)(h * ATT_D) * ld_vt + start;
+  u32x4 rk[2], rv[2];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + 256 * i;
+      const int key = c >> 3, ch = c & 7;
+      rk[i] = *(const u32x4*)(kbase + (int64_t)(start + min(k0 + key, len - 1)) * ld_qk + ch * 8);
+      const int e = c >> 3, kc = c & 7;
+      u32x4 v = *(const u32x4*)(vbase + (int64_t)e * ld_vt + k0 + kc * 8);
+      const int first = k0 + kc * 8;
+      if (first + 8 > len) {            // ragged end: zero the values of keys past the clip
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          uint32_t word = v[w];
+          if (first + 2 * w >= len) word &= 0xFFFF0000u;
+          if (first + 2 * w + 1 >= len) word &= 0x0000FFFFu;
+          v[w] = word;
+        }
+      }
+      rv[i] = v;
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + 256 * i;
+      const int key = c >> 3, ch = c & 7;
+      *(u32x4*)(&Ks[buf][key * ATT_D + att_swz(key, ch) * 8]) = rk[i];
+      // Keys 8kc .. 8kc+7 are two groups of four; within each 16-key block the
+      // groups are stored in the order (0, 2, 1, 3) so that lane half 0 reads
+      // keys {0-3, 8-11} and lane half 1 reads {4-7, 12-15} as one 16-byte chunk.
+      const int e = c >> 3, kc = c & 7;
+      const int blk = 16 * (kc >> 1);
+      const int p_lo = blk + ((kc & 1) ? 4 : 0);
+      const int p_hi = blk + ((kc & 1) ? 12 : 8);
+      bf16_t* row = &Vs[buf][e * ATT_BK];
+      *(u32x2*)(row + att_swz(e, p_lo >> 3) * 8 + (p_lo & 7)) = u32x2{rv[i][0], rv[i][1]};
+      *(u32x2*)(row + att_swz(e, p_hi >> 3) * 8 + (p_hi & 7)) = u32x2{rv[i][2], rv[i][3]};
+    }
+  };
+
+  const float c = 0.125f * 1.44269504088896341f;           // 1/sqrt(64) * log2(e)
+  float m_run = -INFINITY, l_run = 0.0f;
+  f32x16 oacc[2];
+#pragma unroll
+  for (int es = 0; es < 2; ++es)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) oacc[es][v] = 0.0f;
+
+  const int n_tiles = (len + ATT_BK - 1) / ATT_BK;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+
+  for (int kt = 0; kt < n_tiles; ++kt) {
+    const int buf = kt & 1;
+    const int k0 = kt * ATT_BK;
+    if (kt + 1 < n_tiles) gload(k0 + ATT_BK);
+
+    // ---- S^T = K Q^T for two 32-key sub-tiles ----
+    f32x16 s[2];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s[sub][v] = 0.0f;
+      const int key = 32 * sub + fq;
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const bf16x8 kf = *(const bf16x8*)(&Ks[buf][key * ATT_D + att_swz(key, 2 * st + hh) * 8]);
+        s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[st], s[sub], 0, 0, 0);
+      }
+    }
+    // lane holds keys 32 sub + 8 (v >> 2) + 4 hh + (v & 3) of query qi
+    if (k0 + ATT_BK > len) {
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int key = k0 + 32 * sub + 8 * (v >> 2) + 4 * hh + (v & 3);
+          if (key >= len) s[sub][v] = -INFINITY;
+        }
+    }
+    float mx = s[0][0];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[sub][v]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+    const float mc = m_new * c;
+    m_run = m_new;
+
+    float lsum = 0.0f;
+    bf16x8 pb[2][2];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[sub][8 * u + j], c, -mc));
+          lsum += p;
+          pb[sub][u][j] = (__bf16)p;
+        }
+    l_run = l_run * alpha + lsum;
+#pragma unroll
+    for (int es = 0; es < 2; ++es)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) oacc[es][v] *= alpha;
+
+    // ---- O^T += V^T P^T ----
+#pragma unroll
+    for (int es = 0; es < 2; ++es) {
+      const int e = 32 * es + fq;
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const bf16x8 vf = *(const bf16x8*)(&Vs[buf][e * ATT_BK + att_swz(e, 4 * sub + 2 * u + hh) * 8]);
+          oacc[es] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[sub][u], oacc[es], 0, 0, 0);
+        }
+    }
+
+    if (kt + 1 < n_tiles) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float inv = 1.0f / l_tot;
+  if (qi < len) {
+    bf16_t* orow = o + (int64_t)(start + qi) * ld_o + h * ATT_D;
+#pragma unroll
+    for (int es = 0; es < 2; ++es)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e0 = 32 * es + 8 * i + 4 * hh;
+        u32x2 w;
+        w.x = pack_bf16x2(oacc[es][4 * i + 0] * inv, oacc[es][4 * i + 1] * inv);
+        w.y = pack_bf16x2(oacc[es][4 * i + 2] * inv, oacc[es][4 * i + 3] * inv);
+        *(u32x2*)(orow + e0) = w;
+      }
+  }
+}
+
+hipError_t attention_bf16(const bf16_t* qk, int64_t ld_qk, const bf16_t* vt, int64_t ld_vt, const int32_t* start,
+                          const int32_t* len, int n_clips, int max_len, int n_heads, bf16_t* o, int64_t ld_o,
+                          hipStream_t stream) {
+  if (n_clips <= 0 || max_len <= 0 || n_heads <= 0) return hipErrorInvalidValue;
+  dim3 grid((max_len + ATT_BQ - 1) / ATT_BQ, n_heads, n_clips);
+  hipLaunchKernelGGL(attention_bf16_kernel, grid, dim3(256), 0, stream, qk, ld_qk, vt, ld_vt, start, len,
+                     n_heads * ATT_D, o, ld_o);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// fp32 path: one thread per query, 64-key tiles of K and V in LDS, online
+// softmax with one rescale per tile.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void attention_f32_kernel(const float* __restrict__ qkv, int64_t ld,
+                                                           const int32_t* __restrict__ starts,
+                                                           const int32_t* __restrict__ lens, int d,
+                                                           float* __restrict__ o, int64_t ld_o) {
+  __shared__ float Ks[ATT_BK][ATT_D + 1];
+  __shared__ float Vs[ATT_BK][ATT_D + 1];
+  const int b = blockIdx.z, h = blockIdx.y;
+  const int start = starts[b];
+  const int len = lens[b];
+  const int q0 = blockIdx.x * 64;
+  if (q0 >= len) return;
+  const int t = threadIdx.x;
+  const int qi = min(q0 + t, len - 1);
+  float q[ATT_D], acc[ATT_D];
+  const float* qrow = qkv + (int64_t)(start + qi) * ld + h * ATT_D;
+#pragma unroll
+  for (int e = 0; e < ATT_D; ++e) { q[e] = qrow[e] * 0.125f; acc[e] = 0.0f; }
+  float m_run = -INFINITY, l_run = 0.0f;
+  for (int k0 = 0; k0 < len; k0 += ATT_BK) {
+    __syncthreads();
+    for (int i = t; i < ATT_BK * ATT_D; i += 64) {
+      const int key = i / ATT_D, e = i % ATT_D;
+      const int64_t row = (int64_t)(start + min(k0 + key, len - 1)) * ld;
+      Ks[key][e] = qkv[row + d + h * ATT_D + e];
+      Vs[key][e] = qkv[row + 2 * d + h * ATT_D + e];
+    }
+    __syncthreads();
+    const int nk = min(ATT_BK, len - k0);
+    float s[ATT_BK];
+    float mx = -INFINITY;
+    for (int j = 0; j < ATT_BK; ++j) {
+      float v = 0.0f;
+#pragma unroll
+      for (int e = 0; e < ATT_D; ++e) v = fmaf(q[e], Ks[j][e], v);
+      s[j] = j < nk ? v : -INFINITY;
+      mx = fmaxf(mx, s[j]);
+    }
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = expf(m_run - m_new);
+    l_run *= alpha;
+#pragma unroll
+    for (int e = 0; e < ATT_D; ++e) acc[e] *= alpha;
+    for (int j = 0; j < nk; ++j) {
+      const float p = expf(s[j] - m_new);
+      l_run += p;
+#pragma unroll
+      for (int e = 0; e < ATT_D; ++e) acc[e] = fmaf(p, Vs[j][e], acc[e]);
+    }
+    m_run = m_new;
+  }
+  if (q0 + t < len) {
+    float* orow = o + (int64_t)(start + q0 + t) * ld_o + h * ATT_D;
+    const float inv = 1.0f / l_run;
+#pragma unroll
+    for (int e = 0; e < ATT_D; ++e) orow[e] = acc[e] * inv;
+  }
+}
+
+hipError_t attention_f32(const float* qkv, int64_t ld, const int32_t* start, const int32_t* len, int n_clips,
+                         int max_len, int n_heads, float* o, int64_t ld_o, hipStream_t stream) {
+  if (n_clips <= 0 || max_len <= 0 || n_heads <= 0) return hipErrorInvalidValue;
+  dim3 grid((max_len + 63) / 64, n_heads, n_clips);
+  hipLaunchKernelGGL(attention_f32_kernel, grid, dim3(64), 0, stream, qkv, ld, start, len, n_heads * ATT_D, o,
+                     ld_o);
+  return hipGetLastError();
+}
+
+}  // namespace aenc

@@ -1,0 +1,72 @@
+// Host-side launchers of the library's kernels (internal to the library).
+#pragma once
+
+#include "common.h"
+#include "epilogue.h"
+
+namespace aenc {
+
+enum GemmTile { GEMM_TILE_256x256 = 0, GEMM_TILE_256x128 = 1, GEMM_TILE_128x128 = 2 };
+
+// bf16 MFMA GEMM, C = epi(A W^T + b); K % 64 == 0.
+hipError_t gemm_bf16(int epi, const bf16_t* A, RowMap arow, const bf16_t* W, int64_t ldw, int M, int N, int K,
+                     const int32_t* m_dev, const EpiParams& ep, int tile_cfg, hipStream_t stream);
+
+// fp32 GEMM on the vector ALUs (the fp32 path), same epilogues; K % 16 == 0.
+hipError_t gemm_f32(int epi, const float* A, RowMap arow, const float* W, int64_t ldw, int M, int N, int K,
+                    const int32_t* m_dev, const EpiParams& ep, hipStream_t stream);
+
+// Bidirectional attention, bf16, head_dim 64. qk: [rows, ld_qk] with Q of head h at
+// column h*64 and K at column d + h*64; vt: V transposed, row (h*64 + e) holds
+// feature e of head h for every packed row, ld_vt apart. Clip b owns packed rows
+// [start[b], start[b] + len[b]); start[b] % 8 == 0. o: [rows, ld_o] bf16, head h at column h*64.
+hipError_t attention_bf16(const bf16_t* qk, int64_t ld_qk, const bf16_t* vt, int64_t ld_vt,
+                          const int32_t* start, const int32_t* len, int n_clips, int max_len, int n_heads,
+                          bf16_t* o, int64_t ld_o, hipStream_t stream);
+
+// The same for the fp32 path with row-major V: qkv [rows, 3d] (Q | K | V).
+hipError_t attention_f32(const float* qkv, int64_t ld, const int32_t* start, const int32_t* len, int n_clips,
+                         int max_len, int n_heads, float* o, int64_t ld_o, hipStream_t stream);
+
+// LayerNorm of fp32 rows: y[r] = LN(x[r]) for r < M (M = *m_dev if set).
+hipError_t layernorm(const float* x, const float* gamma, const float* beta, void* y, int y_dtype, int M,
+                     const int32_t* m_dev, int d, float eps, hipStream_t stream);
+
+// Final LayerNorm written to the output layout [B, T_out, d]: output row (b, j)
+// reads packed row map[b*T + j] (pool 1) or the mean of LN rows map[b*T + 2j]
+// and map[b*T + 2j + 1] (pool 2); rows whose sources are masked become zeros.
+hipError_t final_ln_out(const float* x, const int32_t* map, const float* gamma, const float* beta, void* out,
+                        int out_dtype, int B, int T, int pool, int d, float eps, hipStream_t stream);
+
+// Zero the output rows of masked positions: out row i (of B*T) when map[i] < 0.
+hipError_t zero_masked_rows(const int32_t* map, void* out, int out_dtype, int rows, int width,
+                            hipStream_t stream);
+
+// mel [B, C, F] -> melT [B, F + 2, C_pad] (channels last, one zero frame on each
+// side, channels >= C zero); also zero the two pad frames of g1 [B, F + 2, d].
+hipError_t mel_transpose(const void* mel, int in_dtype, void* melT, int B, int C, int C_pad, int F,
+                         void* g1, int g1_dtype, int d, hipStream_t stream);
+
+// Key mask [B, T] -> row_map [B*T] (packed row or -1), inv_map [B*round_up(T,8)]
+// (packed row -> b*T + t; -1 in alignment gaps), cu [B + 1] (clip starts, multiples
+// of 8; cu[B] = end of the last clip), lens [B] (valid positions per clip),
+// m_valid [1] (= cu[B]). mask = null: all valid.
+hipError_t build_row_maps(const uint8_t* mask, int B, int T, int32_t* row_map, int32_t* inv_map, int32_t* cu,
+                          int32_t* lens, int32_t* m_valid, hipStream_t stream);
+
+// Repack conv weight [out, in, 3] (dtype) -> [out, 3, in_pad] in the same dtype.
+hipError_t repack_conv(const void* src, int dtype, void* dst, int out, int in, int in_pad, hipStream_t stream);
+
+// Convert n elements (dtype) to fp32; src = null fills `fill`.
+hipError_t to_f32(const void* src, int dtype, float* dst, int64_t n, float fill, hipStream_t stream);
+
+// Sinusoidal position table [T, d] fp32.
+hipError_t position_table(float* pe, int T, int d, hipStream_t stream);
+
+// y = GELU(x) elementwise (fp32), for tests of the device erf.
+hipError_t gelu_f32(const float* x, float* y, int64_t n, hipStream_t stream);
+
+// Plain device copy kernel (16-byte vectors), for calibrating traffic counters.
+hipError_t copy_bytes(void* dst, const void* src, int64_t bytes, hipStream_t stream);
+
+}  // namespace aenc

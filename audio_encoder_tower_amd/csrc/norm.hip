@@ -1,0 +1,168 @@
+// LayerNorm kernels: pre-LN of each block and the final LayerNorm (with the
+// optional pair-average pool and the scatter back to the [B, T_out, d] layout).
+//
+// LN(x) = gamma * (x - mean) / sqrt(var + eps) + beta over the d features of a
+// row, biased variance. These kernels are bound by HBM bandwidth: one wave64
+// per row, fp32 rows read once as 16-byte vectors and held in registers for
+// the two reductions (mean, then the centred second moment), then written
+// once (bf16 or fp32).
+#include "common.h"
+#include "launch.h"
+
+namespace aenc {
+
+constexpr int LN_MAXV = 8;   // float4 per lane: d <= 64 * 4 * 8 = 2048
+
+struct RowStats {
+  float mean, rstd;
+};
+
+__device__ __forceinline__ RowStats row_stats(const float4 (&v)[LN_MAXV], int n4, int lane, int d, float eps) {
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < LN_MAXV; ++i)
+    if (lane + 64 * i < n4) s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+  const float mean = wave_sum(s) / (float)d;
+  float q = 0.0f;
+#pragma unroll
+  for (int i = 0; i < LN_MAXV; ++i)
+    if (lane + 64 * i < n4) {
+      const float a = v[i].x - mean, b = v[i].y - mean, c = v[i].z - mean, e = v[i].w - mean;
+      q += (a * a + b * b) + (c * c + e * e);
+    }
+  const float var = wave_sum(q) / (float)d;
+  return RowStats{mean, 1.0f / sqrtf(var + eps)};
+}
+
+__device__ __forceinline__ void load_row(const float* x, float4 (&v)[LN_MAXV], int n4, int lane) {
+#pragma unroll
+  for (int i = 0; i < LN_MAXV; ++i)
+    if (lane + 64 * i < n4) v[i] = ((const float4*)x)[lane + 64 * i];
+}
+
+__device__ __forceinline__ float4 norm4(float4 x, const RowStats& st, float4 g, float4 b) {
+  return make_float4((x.x - st.mean) * st.rstd * g.x + b.x, (x.y - st.mean) * st.rstd * g.y + b.y,
+                     (x.z - st.mean) * st.rstd * g.z + b.z, (x.w - st.mean) * st.rstd * g.w + b.w);
+}
+
+__device__ __forceinline__ void store4(float* y, int j, float4 v) { ((float4*)y)[j] = v; }
+__device__ __forceinline__ void store4(bf16_t* y, int j, float4 v) {
+  u32x2 w;
+  w.x = pack_bf16x2(v.x, v.y);
+  w.y = pack_bf16x2(v.z, v.w);
+  ((u32x2*)y)[j] = w;
+}
+
+template <typename TO>
+__global__ __launch_bounds__(256) void layernorm_kernel(const float* __restrict__ x, const float* __restrict__ gamma,
+                                                        const float* __restrict__ beta, TO* __restrict__ y,
+                                                        int M_arg, const int32_t* m_dev, int d, float eps) {
+  const int M = m_dev ? *m_dev : M_arg;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;
+  const int lane = threadIdx.x & 63, n4 = d >> 2;
+  float4 v[LN_MAXV];
+  load_row(x + (int64_t)row * d, v, n4, lane);
+  const RowStats st = row_stats(v, n4, lane, d, eps);
+  TO* yr = y + (int64_t)row * d;
+#pragma unroll
+  for (int i = 0; i < LN_MAXV; ++i) {
+    const int j = lane + 64 * i;
+    if (j < n4) store4(yr, j, norm4(v[i], st, ((const float4*)gamma)[j], ((const float4*)beta)[j]));
+  }
+}
+
+hipError_t layernorm(const float* x, const float* gamma, const float* beta, void* y, int y_dtype, int M,
+                     const int32_t* m_dev, int d, float eps, hipStream_t stream) {
+  if (d % 4 != 0 || d > 64 * 4 * LN_MAXV || M <= 0) return hipErrorInvalidValue;
+  dim3 grid((M + 3) / 4);
+  if (y_dtype == 1)
+    hipLaunchKernelGGL(layernorm_kernel<bf16_t>, grid, dim3(256), 0, stream, x, gamma, beta, (bf16_t*)y, M, m_dev,
+                       d, eps);
+  else
+    hipLaunchKernelGGL(layernorm_kernel<float>, grid, dim3(256), 0, stream, x, gamma, beta, (float*)y, M, m_dev, d,
+                       eps);
+  return hipGetLastError();
+}
+
+// Final LayerNorm into the output layout. Output row (b, j) of B*T_out.
+template <typename TO>
+__global__ __launch_bounds__(256) void final_ln_kernel(const float* __restrict__ x, const int32_t* __restrict__ map,
+                                                       const float* __restrict__ gamma,
+                                                       const float* __restrict__ beta, TO* __restrict__ out, int B,
+                                                       int T, int pool, int d, float eps) {
+  const int t_out = T / pool;
+  const int orow = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (orow >= B * t_out) return;
+  const int b = orow / t_out, j = orow - b * t_out;
+  const int lane = threadIdx.x & 63, n4 = d >> 2;
+  TO* yr = out + (int64_t)orow * d;
+  int src[2];
+  bool ok = true;
+  for (int p = 0; p < pool; ++p) {
+    src[p] = map[(int64_t)b * T + pool * j + p];
+    ok = ok && src[p] >= 0;
+  }
+  if (!ok) {
+#pragma unroll
+    for (int i = 0; i < LN_MAXV; ++i)
+      if (lane + 64 * i < n4) store4(yr, lane + 64 * i, make_float4(0.f, 0.f, 0.f, 0.f));
+    return;
+  }
+  float4 accv[LN_MAXV];
+  for (int p = 0; p < pool; ++p) {
+    float4 v[LN_MAXV];
+    load_row(x + (int64_t)src[p] * d, v, n4, lane);
+    const RowStats st = row_stats(v, n4, lane, d, eps);
+#pragma unroll
+    for (int i = 0; i < LN_MAXV; ++i) {
+      const int jj = lane + 64 * i;
+      if (jj < n4) {
+        const float4 y = norm4(v[i], st, ((const float4*)gamma)[jj], ((const float4*)beta)[jj]);
+        if (p == 0) accv[i] = y;
+        else accv[i] = make_float4(accv[i].x + y.x, accv[i].y + y.y, accv[i].z + y.z, accv[i].w + y.w);
+      }
+    }
+  }
+  const float scale = pool == 2 ? 0.5f : 1.0f;
+#pragma unroll
+  for (int i = 0; i < LN_MAXV; ++i) {
+    const int jj = lane + 64 * i;
+    if (jj < n4)
+      store4(yr, jj, make_float4(accv[i].x * scale, accv[i].y * scale, accv[i].z * scale, accv[i].w * scale));
+  }
+}
+
+hipError_t final_ln_out(const float* x, const int32_t* map, const float* gamma, const float* beta, void* out,
+                        int out_dtype, int B, int T, int pool, int d, float eps, hipStream_t stream) {
+  if (d % 4 != 0 || d > 64 * 4 * LN_MAXV || (pool != 1 && pool != 2)) return hipErrorInvalidValue;
+  const int rows = B * (T / pool);
+  if (rows <= 0) return hipSuccess;
+  dim3 grid((rows + 3) / 4);
+  if (out_dtype == 1)
+    hipLaunchKernelGGL(final_ln_kernel<bf16_t>, grid, dim3(256), 0, stream, x, map, gamma, beta, (bf16_t*)out, B, T,
+                       pool, d, eps);
+  else
+    hipLaunchKernelGGL(final_ln_kernel<float>, grid, dim3(256), 0, stream, x, map, gamma, beta, (float*)out, B, T,
+                       pool, d, eps);
+  return hipGetLastError();
+}
+
+template <typename TO>
+__global__ void zero_rows_kernel(const int32_t* __restrict__ map, TO* __restrict__ out, int rows, int width) {
+  const int r = blockIdx.x;
+  if (r >= rows || map[r] >= 0) return;
+  for (int i = threadIdx.x; i < width; i += blockDim.x) out[(int64_t)r * width + i] = TO(0);
+}
+
+hipError_t zero_masked_rows(const int32_t* map, void* out, int out_dtype, int rows, int width,
+                            hipStream_t stream) {
+  if (rows <= 0) return hipSuccess;
+  if (out_dtype == 1)
+    hipLaunchKernelGGL(zero_rows_kernel<bf16_t>, dim3(rows), dim3(256), 0, stream, map, (bf16_t*)out, rows, width);
+  else
+    hipLaunchKernelGGL(zero_rows_kernel<float>, dim3(rows), dim3(256), 0, stream, map, (float*)out, rows, width);
+  return hipGetLastError();
+}
+
+}  // namespace aenc

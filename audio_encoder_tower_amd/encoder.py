@@ -1,0 +1,141 @@
+"""Python face of the C ABI: an encoder handle over torch device tensors.
+
+PyTorch provides device memory and streams only; the forward pass is the
+library's kernels, enqueued by aenc_forward on the given stream.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Dict, Optional, Sequence
+
+import torch
+
+from . import _lib
+from ._lib import AencError, check, lib
+
+TORCH_DTYPE = {_lib.AENC_F32: torch.float32, _lib.AENC_BF16: torch.bfloat16}
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the library must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def output_shape(geom) -> Sequence[int]:
+    g = _lib.geometry(geom)
+    shape = (ctypes.c_int64 * 3)()
+    check(lib().aenc_output_shape(ctypes.byref(g), shape), "aenc_output_shape")
+    return tuple(int(s) for s in shape)
+
+
+def param_count(geom) -> int:
+    g = _lib.geometry(geom)
+    n = lib().aenc_param_count(ctypes.byref(g))
+    if n < 0:
+        raise AencError(f"aenc_param_count: {_lib.last_error()}")
+    return int(n)
+
+
+def validate(geom) -> int:
+    g = _lib.geometry(geom)
+    return int(lib().aenc_validate(ctypes.byref(g)))
+
+
+class Encoder:
+    """An encoder on the current HIP device.
+
+    geom: an object with the aenc_geometry fields (batch, n_mel, n_frames,
+      d_model, n_layers, n_heads, d_ffn, pool_step, proj_hidden, proj_out,
+      dtype, out_dtype, ln_eps).
+    weights: name -> tensor (host or device, contiguous, the geometry's
+      dtype); names conv1_w, conv1_b, conv2_w, conv2_b,
+      layers.{l}.{ln1_g, ln1_b, q_w, q_b, k_w, v_w, v_b, o_w, o_b, ln2_g, ln2_b,
+      fc1_w, fc1_b, fc2_w, fc2_b}, lnf_g, lnf_b and proj{1,2}_{w,b}. Missing
+      biases and betas are zero, missing gammas one.
+    The library copies the weights; they may be freed after construction.
+    """
+
+    def __init__(self, geom, weights: Dict[str, torch.Tensor]):
+        self.geom = geom
+        self._g = _lib.geometry(geom)
+        check(lib().aenc_validate(ctypes.byref(self._g)), "aenc_validate")
+        self.dtype = TORCH_DTYPE[self._g.dtype]
+        self.out_dtype = TORCH_DTYPE[self._g.out_dtype]
+        keep = []
+
+        def p(name):
+            t = weights.get(name)
+            if t is None:
+                return None
+            t = t.contiguous()
+            if t.dtype != self.dtype:
+                raise ValueError(f"{name}: dtype {t.dtype}, expected {self.dtype}")
+            keep.append(t)
+            return t.data_ptr()
+
+        layers = (_lib.LayerWeights * max(1, geom.n_layers))()
+        for layer in range(geom.n_layers):
+            for f in _lib.LAYER_FIELDS:
+                setattr(layers[layer], f, p(f"layers.{layer}.{f}"))
+        w = _lib.Weights(conv1_w=p("conv1_w"), conv1_b=p("conv1_b"), conv2_w=p("conv2_w"), conv2_b=p("conv2_b"),
+                         layers=layers, lnf_g=p("lnf_g"), lnf_b=p("lnf_b"), proj1_w=p("proj1_w"),
+                         proj1_b=p("proj1_b"), proj2_w=p("proj2_w"), proj2_b=p("proj2_b"))
+        h = lib().aenc_create(ctypes.byref(self._g), ctypes.byref(w))
+        if not h:
+            raise AencError(f"aenc_create: {_lib.last_error()}")
+        self._h = ctypes.c_void_p(h)
+        self.out_shape = output_shape(geom)
+
+    def forward(self, mel: torch.Tensor, mask: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                stream=None) -> torch.Tensor:
+        """Enqueue one forward on `stream` (default: torch's current stream)."""
+        g = self._g
+        T = g.n_frames // 2
+        if tuple(mel.shape) != (g.batch, g.n_mel, g.n_frames) or mel.dtype != self.dtype or not mel.is_cuda:
+            raise ValueError(f"mel must be a device tensor {self.dtype} of shape {(g.batch, g.n_mel, g.n_frames)}")
+        if mask is not None:
+            if tuple(mask.shape) != (g.batch, T) or mask.dtype != torch.uint8 or not mask.is_cuda:
+                raise ValueError(f"mask must be a device uint8 tensor of shape {(g.batch, T)}")
+        if out is None:
+            out = torch.empty(self.out_shape, dtype=self.out_dtype, device=mel.device)
+        elif tuple(out.shape) != self.out_shape or out.dtype != self.out_dtype or not out.is_cuda:
+            raise ValueError(f"out must be a device tensor {self.out_dtype} of shape {self.out_shape}")
+        st = lib().aenc_forward(self._h, _ptr(mel), _ptr(mask), _ptr(out), _stream_handle(stream))
+        check(st, "aenc_forward")
+        return out
+
+    __call__ = forward
+
+    # -- per-step timing -------------------------------------------------
+    def profile(self, on: bool = True) -> None:
+        check(lib().aenc_profile_enable(self._h, int(on)), "aenc_profile_enable")
+
+    def profile_read(self) -> Dict[str, tuple]:
+        """{kind: (total ms, launches)} over the forwards since the last read."""
+        n = lib().aenc_profile_kind_count()
+        ms = (ctypes.c_double * n)()
+        calls = (ctypes.c_int64 * n)()
+        got = lib().aenc_profile_read(self._h, ms, calls, n)
+        if got < 0:
+            check(got, "aenc_profile_read")
+        return {lib().aenc_profile_kind_name(k).decode(): (ms[k], calls[k]) for k in range(n) if calls[k]}
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            lib().aenc_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

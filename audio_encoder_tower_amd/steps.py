@@ -1,0 +1,91 @@
+"""Single steps of the tower (include/aenc_kernels.h) on torch device tensors.
+
+Marshalling only: shapes are checked here, the work is one library kernel
+enqueued on torch's current stream.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import torch
+
+from ._lib import check, lib
+
+EPI = {"bf16": 0, "gelu_bf16": 1, "resid_f32": 2, "f32": 3}
+TILE = {"auto": -1, "256x256": 0, "256x128": 1, "128x128": 2}
+
+
+def _p(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    assert t.is_cuda and t.is_contiguous(), "device contiguous tensors only"
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _s():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def gemm_bf16(epi: str, a: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor], c: torch.Tensor,
+              tile: str = "auto") -> torch.Tensor:
+    """c = epi(a w^T + bias); a [M, K] bf16, w [N, K] bf16, bias fp32 [N]."""
+    M, K = a.shape
+    N = w.shape[0]
+    assert a.dtype == w.dtype == torch.bfloat16 and w.shape[1] == K and c.shape == (M, N)
+    assert bias is None or (bias.dtype == torch.float32 and bias.numel() == N)
+    check(lib().aenc_k_gemm_bf16(EPI[epi], _p(a), K, _p(w), _p(bias), _p(c), N, M, N, K, TILE[tile], _s()),
+          "aenc_k_gemm_bf16")
+    return c
+
+
+def qkv_bf16(a: torch.Tensor, wqkv: torch.Tensor, bias: Optional[torch.Tensor], qk: torch.Tensor,
+             vt: torch.Tensor) -> None:
+    M, d = a.shape
+    assert wqkv.shape == (3 * d, d) and qk.shape == (M, 2 * d) and vt.shape[0] == d
+    check(lib().aenc_k_qkv_bf16(_p(a), _p(wqkv), _p(bias), _p(qk), _p(vt), vt.shape[1], M, d, _s()),
+          "aenc_k_qkv_bf16")
+
+
+def attention_bf16(qk: torch.Tensor, vt: torch.Tensor, start: torch.Tensor, lens: torch.Tensor, max_len: int,
+                   n_heads: int, out: torch.Tensor) -> torch.Tensor:
+    d = 64 * n_heads
+    assert qk.shape[1] == 2 * d and vt.shape[0] == d and out.shape == (qk.shape[0], d)
+    assert start.dtype == lens.dtype == torch.int32 and start.numel() >= lens.numel()
+    check(lib().aenc_k_attention_bf16(_p(qk), _p(vt), vt.shape[1], _p(start), _p(lens), lens.numel(), max_len,
+                                      n_heads, _p(out), _s()), "aenc_k_attention_bf16")
+    return out
+
+
+def layernorm(x: torch.Tensor, gamma: torch.Tensor, beta: torch.Tensor, y: torch.Tensor, eps: float) -> torch.Tensor:
+    M, d = x.shape
+    assert x.dtype == gamma.dtype == beta.dtype == torch.float32 and y.shape == (M, d)
+    y_code = 1 if y.dtype == torch.bfloat16 else 0
+    check(lib().aenc_k_layernorm(_p(x), _p(gamma), _p(beta), _p(y), y_code, M, d, eps, _s()), "aenc_k_layernorm")
+    return y
+
+
+def gelu_f32(x: torch.Tensor, y: torch.Tensor) -> torch.Tensor:
+    assert x.dtype == y.dtype == torch.float32 and x.numel() == y.numel()
+    check(lib().aenc_k_gelu_f32(_p(x), _p(y), x.numel(), _s()), "aenc_k_gelu_f32")
+    return y
+
+
+def row_maps(mask: Optional[torch.Tensor], B: int, T: int):
+    """Packing maps of a key mask: (row_map, inv_map, cu, lens, m_valid) int32 device tensors."""
+    dev = torch.device("cuda")
+    T8 = (T + 7) // 8 * 8
+    row_map = torch.empty(B * T, dtype=torch.int32, device=dev)
+    inv_map = torch.empty(B * T8, dtype=torch.int32, device=dev)
+    cu = torch.empty(B + 1, dtype=torch.int32, device=dev)
+    lens = torch.empty(B, dtype=torch.int32, device=dev)
+    mv = torch.empty(1, dtype=torch.int32, device=dev)
+    check(lib().aenc_k_row_maps(_p(mask), B, T, _p(row_map), _p(inv_map), _p(cu), _p(lens), _p(mv), _s()),
+          "aenc_k_row_maps")
+    return row_map, inv_map, cu, lens, mv
+
+
+def copy(dst: torch.Tensor, src: torch.Tensor) -> None:
+    nbytes = src.numel() * src.element_size()
+    assert dst.numel() * dst.element_size() >= nbytes
+    check(lib().aenc_k_copy(_p(dst), _p(src), nbytes, _s()), "aenc_k_copy")

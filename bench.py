@@ -1,0 +1,209 @@
+"""Throughput of the audio encoder tower on one MI355X.
+
+A step is one forward of the whole tower (conv stem, positions, every block,
+final LayerNorm and the projector or pool) over one batch of synthetic clips
+already resident in HBM. Prints one JSON line:
+
+  value        audio-seconds encoded per second (30 s per full clip)
+  tflops       algorithmic TFLOP/s, and mfma_frac = tflops / bf16 dense peak
+  roofline     the kernel with the most time, against its own roofline, with
+               its average launch time from HIP events on the forward's stream
+  cpu_baseline the fp64 CPU oracle on a bounded sample of the same workload
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+METRIC = "encoder audio-seconds/sec (30 s chunks, bf16, 1 GPU) + % of bf16 MFMA peak"
+# MI355X published peaks: dense bf16 MFMA 2.5 PFLOP/s, fp32 157.3 TFLOP/s, HBM3E 8 TB/s.
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
+PEAK_HBM_GBS = 8000.0
+
+
+def step_flops(g, kind: str, rows: int) -> float:
+    """Algorithmic FLOPs of one launch of a GEMM-like step over `rows` valid positions."""
+    d, f = g.d_model, g.d_ffn
+    return {
+        "qkv": 2.0 * rows * d * 3 * d,
+        "o_proj": 2.0 * rows * d * d,
+        "fc1": 2.0 * rows * d * f,
+        "fc2": 2.0 * rows * f * d,
+        "proj1": 2.0 * rows * d * g.proj_hidden,
+        "proj2": 2.0 * rows * g.proj_hidden * g.proj_out,
+    }.get(kind, 0.0)
+
+
+def attention_flops(g, tb) -> float:
+    return float(sum(4.0 * t * t * g.d_model for t in tb))
+
+
+def cpu_baseline(w, blocks: int = 4):
+    """Time the oracle (as it is) on one clip: the stem, `blocks` of the blocks,
+    and the final norm (+ projector); block time is scaled to the full depth."""
+    import oracle
+    from oracle import encoder as E
+    g = w.geom
+    W = synth.make_weights(w.replace(geom=g.replace(n_layers=blocks)))
+    Wfull_proj = W
+    mel = synth.make_mel(w, clips=[0])[0]
+    mask = synth.make_mask(w, clips=[0])
+    m = None if mask is None else mask[0]
+    t0 = time.perf_counter()
+    x = E.stem(mel, W)
+    t1 = time.perf_counter()
+    x = E.blocks(x, W, blocks, g.n_heads, m, g.ln_eps)
+    t2 = time.perf_counter()
+    E.final(x, Wfull_proj, g.pool_step, g.ln_eps)
+    t3 = time.perf_counter()
+    per_clip = (t1 - t0) + (t2 - t1) * g.n_layers / blocks + (t3 - t2)
+    frames = synth.make_lengths(w, 1)[0]
+    cores = len(os.sched_getaffinity(0))
+    return {
+        "value": round(float(frames) / 100.0 / per_clip, 4),
+        "unit": "audio-s/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": (f"1 clip of {w.name}: stem + {blocks} of {g.n_layers} blocks + final norm"
+                   f"{' + projector' if g.proj_hidden else ''}, fp64 NumPy; block time scaled x{g.n_layers / blocks:g}; "
+                   f"measured {t3 - t0:.1f} s"),
+        "seconds_per_clip": round(per_clip, 3),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=synth.workloads.HEADLINE)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-blocks", type=int, default=4)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        sys.exit("bench.py runs on one GPU only: the encoder's clips are independent, and this build "
+                 "measures one GPU's share (see the sharding notes); use --gpus 1")
+
+    import torch
+    import audio_encoder_tower_amd as aenc
+
+    assert torch.cuda.is_available(), "no HIP device"
+    w = synth.get_workload(args.workload)
+    g = w.geom
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    tdt = torch.bfloat16 if g.dtype == "bf16" else torch.float32
+
+    W = synth.make_weights(w)
+    enc = aenc.Encoder(g, {k: torch.from_numpy(v).to(dev).to(tdt) for k, v in W.items()})
+    del W
+    mel = torch.from_numpy(synth.make_mel(w)).to(dev).to(tdt)
+    mask_np = synth.make_mask(w)
+    mask = None if mask_np is None else torch.from_numpy(mask_np).to(dev)
+    out = torch.empty(enc.out_shape, dtype=enc.out_dtype, device=dev)
+    stream = torch.cuda.current_stream()
+
+    frames = synth.make_lengths(w)
+    tb = (frames + 1) // 2
+    audio_s = float(frames.sum()) / 100.0
+    import oracle  # closed-form FLOP count only
+    flops = oracle.flops(g, frames)
+
+    for _ in range(args.warmup):
+        enc.forward(mel, mask, out, stream)
+    torch.cuda.synchronize()
+
+    # ---- timed region ----
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        enc.forward(mel, mask, out, stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = start.elapsed_time(end)
+    ms_step = ms_total / args.steps
+
+    # ---- per-kernel times: HIP events around every launch, same stream ----
+    enc.profile(True)
+    for _ in range(args.steps):
+        enc.forward(mel, mask, out, stream)
+    torch.cuda.synchronize()
+    kinds = enc.profile_read()
+    enc.profile(False)
+
+    rows = int(tb.sum())
+    per_kind = {}
+    for k, (ms, n) in sorted(kinds.items(), key=lambda kv: -kv[1][0]):
+        avg = ms / n
+        entry = {"ms_per_step": round(ms / args.steps, 4), "launches_per_step": n // args.steps,
+                 "avg_launch_ms": round(avg, 5)}
+        fl = step_flops(g, k, rows) if k != "attention" else attention_flops(g, tb)
+        if fl:
+            entry["tflops"] = round(fl / (avg * 1e-3) / 1e12, 1)
+        per_kind[k] = entry
+    dominant = max(kinds, key=lambda k: kinds[k][0])
+    dom_ms, dom_n = kinds[dominant]
+    dom_avg = dom_ms / dom_n
+    dom_flops = step_flops(g, dominant, rows) if dominant != "attention" else attention_flops(g, tb)
+    peak = PEAK_TFLOPS[g.dtype]
+    roofline = {
+        "kernel": dominant,
+        "bound": "mfma",
+        "achieved": round(dom_flops / (dom_avg * 1e-3) / 1e12, 1),
+        "peak": peak,
+        "unit": "TFLOP/s",
+        "frac": round(dom_flops / (dom_avg * 1e-3) / 1e12 / peak, 4),
+        "traffic": None,
+        "avg_launch_ms": round(dom_avg, 5),
+        "flops_per_launch": dom_flops,
+    }
+
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    result = {
+        "metric": METRIC,
+        "value": round(audio_s / (ms_step * 1e-3), 1),
+        "unit": "audio-s/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": g.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "global_batch": g.batch, "seq_len": g.n_pos, "mel_frames": g.n_frames,
+                   "d_model": g.d_model, "layers": g.n_layers, "heads": g.n_heads, "ffn": g.d_ffn,
+                   "pool_step": g.pool_step, "projector": [g.proj_hidden, g.proj_out] if g.proj_hidden else None,
+                   "audio_seconds_per_step": audio_s, "parallelism": "none (1 GPU)"},
+        "tflops": round(tflops, 1),
+        "mfma_frac": round(tflops / peak, 4),
+        "flops_per_step": flops,
+        "wall_s_timed": round(wall, 3),
+        "roofline": roofline,
+        "kernels": per_kind,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_blocks)
+    print(json.dumps(result), flush=True)
+    enc.close()
+
+
+if __name__ == "__main__":
+    main()

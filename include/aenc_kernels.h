@@ -1,0 +1,83 @@
+/*
+ * aenc_kernels.h - single steps of the encoder tower, exported for per-step
+ * parity tests and measurement. Each call enqueues one kernel on `stream` (a
+ * hipStream_t, NULL = null stream) and returns without synchronising. All
+ * pointers are device pointers owned by the caller. Return AENC_OK,
+ * AENC_E_INVAL (bad sizes, checked on the host before the launch) or
+ * AENC_E_HIP (the launch failed; aenc_last_error() says why).
+ *
+ * The operations are the pieces of the forward pass declared in aenc.h and
+ * come from the same passages: linear maps with [out, in] weights and the
+ * gelu activation ("Qwen2-Audio-7B-Instruct", (1) AUDIO ENCODER; "Voxtral-
+ * Mini-3B-2507", PROJECTOR), bidirectional multi-head attention with head_dim
+ * 64 ("Voxtral-Mini-3B-2507", (1) AUDIO ENCODER) and the LayerNorms of the
+ * pre-LN blocks.
+ */
+#ifndef AENC_KERNELS_H
+#define AENC_KERNELS_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Epilogues of aenc_k_gemm_bf16. */
+enum {
+  AENC_EPI_BF16 = 0,      /* C (bf16) = A W^T + b                     */
+  AENC_EPI_GELU_BF16 = 1, /* C (bf16) = GELU(A W^T + b), erf form     */
+  AENC_EPI_RESID_F32 = 2, /* C (fp32) += A W^T + b                    */
+  AENC_EPI_F32 = 3        /* C (fp32) = A W^T + b                     */
+};
+
+/* Tile shapes of aenc_k_gemm_bf16 (-1 = the library's choice). */
+enum { AENC_TILE_256x256 = 0, AENC_TILE_256x128 = 1, AENC_TILE_128x128 = 2 };
+
+/* C[M, N] = epi(A[M, K] W[N, K]^T + bias[N]) with bf16 A and W (row-major,
+ * leading dimensions lda, K and ldc in elements), fp32 accumulate.
+ * bias: fp32 [N] or NULL. K must be a positive multiple of 64; lda a multiple
+ * of 8; M, N >= 1. */
+int aenc_k_gemm_bf16(int epi, const void *A, int64_t lda, const void *W, const float *bias, void *C,
+                     int64_t ldc, int M, int N, int K, int tile, void *stream);
+
+/* The QKV projection of a block: [Q | K | V] = A Wqkv^T + bqkv with A bf16
+ * [M, d], Wqkv bf16 [3d, d], bias fp32 [3d] or NULL. Q and K go to qk (bf16
+ * [M, 2d]); V goes transposed to vt (bf16, row e of [d, ld_vt] holds feature
+ * e of every row; ld_vt >= M + 64, a multiple of 8). d = 64 * heads. */
+int aenc_k_qkv_bf16(const void *A, const void *Wqkv, const float *bias, void *qk, void *vt, int64_t ld_vt,
+                    int M, int d, void *stream);
+
+/* Bidirectional attention over packed clips: clip b owns rows
+ * [start[b], start[b] + len[b]) of qk (Q of head h at column 64h, K at column
+ * d + 64h) and the same columns of vt; every start[b] must be a multiple of 8,
+ * every len[b] >= 1 and max_len >= the longest clip; vt must hold 64 columns
+ * past the end of the last clip. out: bf16 [rows, d], head h at column 64h;
+ * rows outside every clip are not written. */
+int aenc_k_attention_bf16(const void *qk, const void *vt, int64_t ld_vt, const int32_t *start, const int32_t *len,
+                          int n_clips, int max_len, int n_heads, void *out, void *stream);
+
+/* y[r] = LayerNorm(x[r]; gamma, beta, eps) for r < M, x fp32 [M, d], y in
+ * y_dtype (0 fp32, 1 bf16); gamma, beta fp32 [d]. d % 4 == 0, d <= 2048. */
+int aenc_k_layernorm(const float *x, const float *gamma, const float *beta, void *y, int y_dtype, int M, int d,
+                     float eps, void *stream);
+
+/* y = GELU(x), fp32, the device's erf form used in every GELU epilogue. */
+int aenc_k_gelu_f32(const float *x, float *y, int64_t n, void *stream);
+
+/* Packing maps of a key mask uint8 [B, T] (NULL = all valid): row_map [B*T]
+ * (packed row or -1), inv_map [B * round_up(T, 8)] (packed row -> b*T + t,
+ * -1 in alignment gaps), cu [B + 1] (clip starts, multiples of 8; cu[B] is the
+ * end of the last clip), lens [B] (valid positions per clip), m_valid [1]
+ * (= cu[B], the packed rows every per-row step covers). */
+int aenc_k_row_maps(const uint8_t *mask, int B, int T, int32_t *row_map, int32_t *inv_map, int32_t *cu,
+                    int32_t *lens, int32_t *m_valid, void *stream);
+
+/* dst = src, `bytes` (a multiple of 16), by a plain streaming kernel: the
+ * reference point for hardware traffic counters. */
+int aenc_k_copy(void *dst, const void *src, int64_t bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AENC_KERNELS_H */

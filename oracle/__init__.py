@@ -7,6 +7,6 @@ path never calls it, and it shares no code with the HIP kernels or their
 host runtime; the two meet only through the seeded inputs of ``synth``.
 """
 from .encoder import (  # noqa: F401
-    gelu, layer_norm, conv1d_k3, sinusoids, linear, attention, block, blocks, stem,
+    gelu, layer_norm, conv1d_k3, sinusoids, linear, attention, attention_core, block, blocks, stem,
     final, encode_clip, encode, param_count, param_shapes, flops,
 )

@@ -115,11 +115,23 @@ def attention(a: np.ndarray, lw: Dict[str, np.ndarray], n_heads: int,
 
     a [T, d] (the LayerNorm output) -> concat_h(O_h) W_o^T + b_o, [T, d].
     """
-    t, d = a.shape
-    dh = d // n_heads
     q = linear(a, _f(lw["q_w"], dtype), _f(lw["q_b"], dtype))
     k = linear(a, _f(lw["k_w"], dtype), None if k_bias is None else _f(k_bias, dtype))
     v = linear(a, _f(lw["v_w"], dtype), _f(lw["v_b"], dtype))
+    o, p = attention_core(q, k, v, n_heads, key_mask)
+    out = linear(o, _f(lw["o_w"], dtype), _f(lw["o_b"], dtype))
+    return (out, p) if return_probs else out
+
+
+def attention_core(q: np.ndarray, k: np.ndarray, v: np.ndarray, n_heads: int,
+                   key_mask: Optional[np.ndarray] = None):
+    """Per head h: softmax_j(Q_h K_h^T / sqrt(dh)) V_h, heads concatenated.
+
+    q, k, v [T, d] -> (o [T, d], probabilities [H, T, T]). Masked keys get
+    probability 0; each row is normalised after subtracting its maximum.
+    """
+    t, d = q.shape
+    dh = d // n_heads
     qh = q.reshape(t, n_heads, dh).transpose(1, 0, 2)
     kh = k.reshape(t, n_heads, dh).transpose(1, 0, 2)
     vh = v.reshape(t, n_heads, dh).transpose(1, 0, 2)
@@ -130,8 +142,7 @@ def attention(a: np.ndarray, lw: Dict[str, np.ndarray], n_heads: int,
     p = np.exp(s)
     p = p / p.sum(axis=-1, keepdims=True)
     o = (p @ vh).transpose(1, 0, 2).reshape(t, d)
-    out = linear(o, _f(lw["o_w"], dtype), _f(lw["o_b"], dtype))
-    return (out, p) if return_probs else out
+    return o, p
 
 
 def block(x: np.ndarray, lw: Dict[str, np.ndarray], n_heads: int,

@@ -1,0 +1,127 @@
+"""Helpers of the GPU parity tests: tolerance checks, device copies of the
+seeded inputs, and oracle outputs (computed, or read back from the cache that
+tests/golden/make_oracle_cache.py writes by calling only the oracle)."""
+from __future__ import annotations
+
+import hashlib
+import inspect
+import json
+import os
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+
+import oracle
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CACHE_DIR = os.path.join(ROOT, "tests", ".oracle_cache")
+
+# Tolerances of the GPU path against the fp64 oracle.
+BF16_MAX_ABS = 3e-2
+BF16_MIN_ROW_COS = 0.999
+F32_MAX_REL = 1e-4
+
+
+def metrics(got: np.ndarray, ref: np.ndarray) -> Dict[str, float]:
+    """max-abs, min row cosine (rows = last axis) and normwise max-rel."""
+    g = np.asarray(got, np.float64).reshape(-1, got.shape[-1])
+    r = np.asarray(ref, np.float64).reshape(-1, ref.shape[-1])
+    diff = np.abs(g - r)
+    num = (g * r).sum(1)
+    den = np.linalg.norm(g, axis=1) * np.linalg.norm(r, axis=1)
+    cos = np.where(den > 0, num / np.maximum(den, 1e-300), 1.0)
+    return {"max_abs": float(diff.max()), "min_row_cos": float(cos.min()),
+            "max_rel": float(diff.max() / max(np.abs(r).max(), 1e-300)),
+            "finite": bool(np.isfinite(g).all())}
+
+
+def assert_bf16_parity(got, ref, what=""):
+    m = metrics(got, ref)
+    assert m["finite"], f"{what}: non-finite output"
+    assert m["max_abs"] <= BF16_MAX_ABS and m["min_row_cos"] >= BF16_MIN_ROW_COS, f"{what}: {m}"
+    return m
+
+
+def assert_f32_parity(got, ref, what=""):
+    m = metrics(got, ref)
+    assert m["finite"], f"{what}: non-finite output"
+    assert m["max_rel"] <= F32_MAX_REL, f"{what}: {m}"
+    return m
+
+
+# ---------------------------------------------------------------------------
+# Oracle outputs, cached per (workload, clip, rows) and keyed on the oracle's source.
+# ---------------------------------------------------------------------------
+
+def _fingerprint(W: dict, mel: np.ndarray, mask) -> str:
+    """Digest of the inputs the oracle reads (strided samples of every tensor)."""
+    h = hashlib.sha256()
+    for name in sorted(W):
+        a = np.ascontiguousarray(W[name], np.float32).ravel()
+        h.update(name.encode() + str(W[name].shape).encode())
+        h.update(a[:: max(1, a.size // 4096)].tobytes())
+    h.update(np.ascontiguousarray(mel, np.float32).tobytes())
+    if mask is not None:
+        h.update(np.ascontiguousarray(mask).tobytes())
+    return h.hexdigest()
+
+
+def _key(w: synth.Workload, clip: int, W: dict, mel: np.ndarray, mask) -> str:
+    spec = json.dumps({"geom": repr(w.geom), "clip": clip, "data": _fingerprint(W, mel, mask),
+                       "oracle": hashlib.sha256(inspect.getsource(oracle.encoder).encode()).hexdigest()},
+                      sort_keys=True)
+    return hashlib.sha256(spec.encode()).hexdigest()[:24]
+
+
+def sample_rows(n: int, every: int) -> np.ndarray:
+    rows = set(range(0, n, every)) | {0, 1, n - 2, n - 1}
+    return np.array(sorted(r for r in rows if 0 <= r < n))
+
+
+def oracle_clip(w: synth.Workload, clip: int, W: Optional[dict] = None, every: int = 1,
+                use_cache: bool = True) -> Dict[str, np.ndarray]:
+    """Oracle output of one clip: {"rows": indices, "out": [len(rows), D_out]} (fp64).
+
+    The clip runs alone (clips are independent) with its own mask row. The
+    cache key covers the geometry, a digest of the weights and inputs and the
+    oracle's source, so a stale entry is never read.
+    """
+    if W is None:
+        W = synth.make_weights(w)
+    mel = synth.make_mel(w, clips=[clip])[0]
+    mask = synth.make_mask(w, clips=[clip])
+    path = os.path.join(CACHE_DIR, f"{w.name}-{_key(w, clip, W, mel, mask)}-e{every}.npz")
+    if use_cache and os.path.exists(path):
+        with np.load(path) as z:
+            return {"rows": z["rows"], "out": z["out"].astype(np.float64)}
+    out = oracle.encode_clip(w.geom, W, mel, None if mask is None else mask[0])
+    rows = sample_rows(out.shape[0], every)
+    res = {"rows": rows, "out": out[rows]}
+    if use_cache:
+        os.makedirs(CACHE_DIR, exist_ok=True)
+        np.savez(path + ".tmp.npz", rows=rows, out=res["out"].astype(np.float32))
+        os.replace(path + ".tmp.npz", path)
+        res["out"] = res["out"].astype(np.float32).astype(np.float64)
+    return res
+
+
+# Full-size workloads: which clips and rows the parity tests compare.
+FULL_SIZE_SAMPLES = {
+    "tiny_fp32_b1": dict(clips=[0], every=1),
+    "whisper_medium_pool2_b1": dict(clips=[0], every=1),
+    "whisper_large_b1": dict(clips=[0], every=1),
+    "whisper_large_proj_b16": dict(clips=[0, 15], every=5),
+    "whisper_large_varlen_b32": dict(clips=None, every=5),   # shortest, longest and one in between
+}
+
+
+def varlen_sample_clips(w: synth.Workload) -> Sequence[int]:
+    lengths = synth.make_lengths(w)
+    order = np.argsort(lengths, kind="stable")
+    return sorted({int(order[0]), int(order[len(order) // 2]), int(order[-1])})
+
+
+def full_size_clips(w: synth.Workload) -> Sequence[int]:
+    spec = FULL_SIZE_SAMPLES[w.name]
+    return varlen_sample_clips(w) if spec["clips"] is None else spec["clips"]

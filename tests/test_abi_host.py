@@ -1,0 +1,119 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads and
+exports every declared symbol, geometry validation and the closed forms."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+import oracle
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("aenc.h", "aenc_kernels.h")]
+
+
+@pytest.fixture(scope="module")
+def aenc():
+    import audio_encoder_tower_amd as a
+    a.lib()
+    return a
+
+
+def declared_functions():
+    names = []
+    for h in HEADERS:
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"\b(aenc_\w+)\s*\(", text)
+    return sorted(set(names))
+
+
+def test_headers_compile_as_c_and_cxx():
+    for lang, std in (("c", "-std=c99"), ("c++", "-std=c++17")):
+        for h in HEADERS:
+            subprocess.run(["gcc", "-fsyntax-only", "-Wall", "-Werror", "-x", lang, std, h], check=True)
+
+
+def test_library_exports_every_declared_symbol(aenc):
+    names = declared_functions()
+    assert len(names) >= 18
+    missing = [n for n in names if not hasattr(aenc.lib(), n)]
+    assert not missing, missing
+    # and the binding gives each a signature
+    from audio_encoder_tower_amd._lib import SIGNATURES
+    assert set(names) == set(SIGNATURES)
+
+
+@pytest.mark.parametrize("name", sorted(synth.WORKLOADS))
+def test_workloads_validate_and_match_closed_forms(aenc, name):
+    g = synth.get_workload(name).geom
+    assert aenc.validate(g) == 0
+    assert aenc.param_count(g) == oracle.param_count(g)
+    assert aenc.output_shape(g) == (g.batch, g.t_out, g.d_out)
+    gg = aenc._lib.geometry(g)
+    assert aenc.lib().aenc_workspace_bytes(ctypes.byref(gg)) > 0
+
+
+BAD = {
+    "batch0": dict(batch=0),
+    "odd_frames": dict(n_frames=301),
+    "too_many_frames": dict(n_frames=3002),
+    "head_dim_not_64": dict(n_heads=5),
+    "d_not_mult_128": dict(d_model=192, n_heads=3),
+    "ffn_not_mult_64": dict(d_ffn=1000),
+    "pool3": dict(pool_step=3),
+    "proj_half": dict(proj_hidden=64, proj_out=0),
+    "bad_dtype": dict(dtype="f16"),
+    "eps0": dict(ln_eps=0.0),
+    "eps_nan": dict(ln_eps=float("nan")),
+    "neg_layers": dict(n_layers=-1),
+}
+
+
+@pytest.mark.parametrize("case", sorted(BAD))
+def test_invalid_geometries_are_rejected(aenc, case):
+    g = synth.get_workload("whisper_large_b1").geom
+    kw = dict(BAD[case])
+    if kw.get("dtype") == "f16":
+        gg = aenc._lib.geometry(g)
+        gg.dtype = 7
+        assert aenc.lib().aenc_validate(ctypes.byref(gg)) == -1
+        return
+    assert aenc.validate(g.replace(**kw)) == -1, case
+    assert aenc.last_error()
+    assert aenc.lib().aenc_param_count(ctypes.byref(aenc._lib.geometry(g.replace(**kw)))) == -1
+
+
+def test_pool_with_projector_is_unsupported(aenc):
+    g = synth.get_workload("whisper_medium_pool2_b1").geom.replace(proj_hidden=128, proj_out=128)
+    assert aenc.validate(g) == -2
+    assert "pool" in aenc.last_error()
+
+
+def test_null_arguments(aenc):
+    L = aenc.lib()
+    assert L.aenc_validate(None) == -1
+    assert L.aenc_create(None, None) is None
+    assert L.aenc_forward(None, None, None, None, None) == -1
+    L.aenc_destroy(None)
+    g = aenc._lib.geometry(synth.get_workload("tiny_fp32_b1").geom)
+    assert L.aenc_create(ctypes.byref(g), None) is None
+    assert "weights" in aenc.last_error()
+    assert L.aenc_output_shape(ctypes.byref(g), None) == -1
+    assert L.aenc_k_gemm_bf16(0, None, 0, None, None, None, 0, 1, 1, 64, -1, None) == -1
+    assert L.aenc_k_copy(None, None, 16, None) == -1
+    # kernel entry points reject bad sizes before any launch
+    buf = ctypes.c_void_p(16)
+    assert L.aenc_k_gemm_bf16(0, buf, 64, buf, None, buf, 64, 64, 64, 100, -1, None) == -1
+    assert L.aenc_k_layernorm(buf, buf, buf, buf, 0, 4, 4096, 1e-5, None) == -1
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the path taken when no device exists")
+def test_create_without_device_reports_it(aenc):
+    w = synth.get_workload("tiny_fp32_b1")
+    W = {k: torch.from_numpy(v) for k, v in synth.make_weights(w).items()}
+    with pytest.raises(aenc.AencError, match="no HIP device"):
+        aenc.Encoder(w.geom, W)

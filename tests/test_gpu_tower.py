@@ -1,0 +1,224 @@
+"""End-to-end parity of the HIP tower (through include/aenc.h) with the oracle.
+
+Reduced geometries are compared element by element on every row; the five
+full-size workloads are compared on sampled clips (each run alone by the
+oracle, clips being independent) and, for the larger ones, sampled rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def aenc():
+    import audio_encoder_tower_amd as a
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    a.lib()
+    return a
+
+
+def device_weights(W, dtype):
+    tdt = torch.bfloat16 if dtype == synth.workloads.BF16 else torch.float32
+    return {k: torch.from_numpy(np.ascontiguousarray(v)).to(DEV).to(tdt) for k, v in W.items()}
+
+
+def run_gpu(aenc, w, W=None, mel=None, mask=None, clips=None):
+    g = w.geom
+    if W is None:
+        W = synth.make_weights(w)
+    if mel is None:
+        mel = synth.make_mel(w, clips=clips)
+        mask = synth.make_mask(w, clips=clips)
+    print(f"gpu forward {w.name} geom={g}", flush=True)
+    enc = aenc.Encoder(g, device_weights(W, g.dtype))
+    tdt = torch.bfloat16 if g.dtype == synth.workloads.BF16 else torch.float32
+    mel_d = torch.from_numpy(mel).to(DEV).to(tdt)
+    mask_d = None if mask is None else torch.from_numpy(mask).to(DEV)
+    out = enc.forward(mel_d, mask_d)
+    torch.cuda.synchronize()
+    res = out.float().cpu().numpy().astype(np.float64)
+    enc.close()
+    return res
+
+
+def tiny(name="tiny_fp32_b1", **kw):
+    w = synth.get_workload(name)
+    return w.replace(geom=w.geom.replace(**kw))
+
+
+def reduced(base, name, geom_kw, **wkw):
+    w = synth.get_workload(base)
+    return w.replace(name=name, geom=w.geom.replace(**geom_kw), **wkw)
+
+
+REDUCED = {
+    # Whisper-large width, 2 blocks, 700 positions (ragged against 64/128/256 tiles), 2 clips
+    "large_width_ragged": reduced("whisper_large_b1", "large_width_ragged",
+                                  dict(n_layers=2, n_frames=1400, batch=2), init="perturbed"),
+    # Whisper-medium width with the pool over an odd number of positions
+    "medium_pool_odd": reduced("whisper_medium_pool2_b1", "medium_pool_odd",
+                               dict(n_layers=2, n_frames=802), init="perturbed"),
+    # projector with a key mask over 3 clips
+    "projector_masked": reduced("whisper_large_b1", "projector_masked",
+                                dict(batch=3, n_layers=1, n_frames=900, d_model=256, n_heads=4, d_ffn=1024,
+                                     proj_hidden=512, proj_out=384), init="perturbed"),
+    # full-width variable-length batch, one block
+    "varlen_large_1block": reduced("whisper_large_varlen_b32", "varlen_large_1block",
+                                   dict(batch=4, n_layers=1)),
+    # sharp attention (Q and K weights std 0.2)
+    "sharp_attention": reduced("whisper_large_b1", "sharp_attention",
+                               dict(n_layers=2, n_frames=600), init="sharp"),
+    # no blocks: stem, positions and final LayerNorm only
+    "no_blocks": reduced("whisper_large_b1", "no_blocks", dict(n_layers=0, batch=2), init="perturbed"),
+    # bf16 output
+    "bf16_out": reduced("whisper_large_b1", "bf16_out", dict(n_layers=1, n_frames=400, out_dtype="bf16"),
+                        init="perturbed"),
+    # the tiny fp32 geometry with nonzero biases and a mask
+    "fp32_perturbed_masked": reduced("tiny_fp32_b1", "fp32_perturbed_masked", dict(batch=3), init="perturbed"),
+    "fp32_projector": reduced("tiny_fp32_b1", "fp32_projector", dict(proj_hidden=128, proj_out=192),
+                              init="perturbed"),
+}
+
+
+# Explicit valid mel frames per clip for some reduced cases (frames past them
+# are zeroed, positions past ceil(n_f / 2) masked).
+LENGTHS = {
+    "projector_masked": [900, 411, 101],
+    "fp32_perturbed_masked": [200, 137, 61],
+}
+
+
+def inputs(w):
+    mel = synth.make_mel(w)
+    mask = synth.make_mask(w)
+    if w.name in LENGTHS:
+        n_f = np.array(LENGTHS[w.name])
+        for b, n in enumerate(n_f):
+            mel[b, :, n:] = 0.0
+        mask = (np.arange(w.geom.n_pos)[None, :] < ((n_f + 1) // 2)[:, None]).astype(np.uint8)
+    return mel, mask
+
+
+def compare(w, got, ref, mask, what):
+    g = w.geom
+    rows = np.ones(got.shape[:2], bool)
+    if mask is not None:
+        t_out = g.t_out
+        valid = mask[:, : t_out * g.pool_step].reshape(mask.shape[0], t_out, g.pool_step).all(-1)
+        rows = valid
+        # masked rows are written as zeros
+        assert np.all(got[~rows] == 0.0), f"{what}: masked rows not zero"
+    if g.dtype == synth.workloads.F32 and g.out_dtype == synth.workloads.F32:
+        return parity.assert_f32_parity(got[rows], ref[rows], what)
+    return parity.assert_bf16_parity(got[rows], ref[rows], what)
+
+
+@pytest.mark.parametrize("case", sorted(REDUCED))
+def test_reduced_tower(aenc, case):
+    w = REDUCED[case]
+    W = synth.make_weights(w)
+    mel, mask = inputs(w)
+    got = run_gpu(aenc, w, W, mel, mask)
+    ref = oracle.encode(w.geom, W, mel, mask)
+    assert got.shape == ref.shape == (w.geom.batch, w.geom.t_out, w.geom.d_out)
+    m = compare(w, got, ref, mask, case)
+    print(case, m)
+
+
+@pytest.mark.parametrize("name", list(parity.FULL_SIZE_SAMPLES))
+def test_full_size_workload(aenc, name):
+    w = synth.get_workload(name)
+    g = w.geom
+    W = synth.make_weights(w)
+    mel = synth.make_mel(w)
+    mask = synth.make_mask(w)
+    got = run_gpu(aenc, w, W, mel, mask)
+    assert got.shape == (g.batch, g.t_out, g.d_out)
+    assert np.isfinite(got).all()
+    every = parity.FULL_SIZE_SAMPLES[name]["every"]
+    for clip in parity.full_size_clips(w):
+        ref = parity.oracle_clip(w, clip, W, every=every)
+        rows = ref["rows"]
+        g_rows = got[clip][rows]
+        clip_mask = None
+        if mask is not None:
+            valid = mask[clip][rows].astype(bool)
+            assert np.all(g_rows[~valid] == 0.0)
+            g_rows, r_rows = g_rows[valid], ref["out"][valid]
+        else:
+            r_rows = ref["out"]
+        if g.dtype == synth.workloads.F32:
+            m = parity.assert_f32_parity(g_rows, r_rows, f"{name} clip {clip}")
+        else:
+            m = parity.assert_bf16_parity(g_rows, r_rows, f"{name} clip {clip}")
+        print(name, clip, m, flush=True)
+
+
+def test_deterministic_and_batch_independent(aenc):
+    w = reduced("whisper_large_varlen_b32", "det", dict(batch=3, n_layers=2, n_frames=1000), init="perturbed")
+    W = synth.make_weights(w)
+    mel = synth.make_mel(w)
+    mask = synth.make_mask(w)
+    a = run_gpu(aenc, w, W, mel, mask)
+    b = run_gpu(aenc, w, W, mel, mask)
+    np.testing.assert_array_equal(a, b)
+    one = w.replace(geom=w.geom.replace(batch=1))
+    c = run_gpu(aenc, one, W, mel[1:2], mask[1:2])
+    np.testing.assert_array_equal(a[1], c[0])
+
+
+def test_padded_frames_do_not_change_valid_rows(aenc):
+    w = reduced("whisper_large_varlen_b32", "pad", dict(batch=2, n_layers=2, n_frames=1200), init="perturbed")
+    W = synth.make_weights(w)
+    mel = synth.make_mel(w)
+    mask = synth.make_mask(w)
+    base = run_gpu(aenc, w, W, mel, mask)
+    junk = mel.copy()
+    rng = np.random.default_rng(0)
+    for b in range(w.geom.batch):
+        tb = int(mask[b].sum())
+        junk[b, :, 2 * tb + 1:] = synth.round_to_bf16(
+            rng.choice([-1e4, 1e4], size=junk[b, :, 2 * tb + 1:].shape).astype(np.float32))
+    other = run_gpu(aenc, w, W, junk, mask)
+    for b in range(w.geom.batch):
+        tb = int(mask[b].sum())
+        np.testing.assert_array_equal(other[b, :tb], base[b, :tb])
+
+
+def test_profile_counts_every_launch(aenc):
+    w = reduced("whisper_large_b1", "prof", dict(n_layers=2, n_frames=400))
+    g = w.geom
+    W = synth.make_weights(w)
+    enc = aenc.Encoder(g, device_weights(W, g.dtype))
+    mel = torch.from_numpy(synth.make_mel(w)).to(DEV).to(torch.bfloat16)
+    enc.profile(True)
+    for _ in range(3):
+        enc.forward(mel)
+    torch.cuda.synchronize()
+    stats = enc.profile_read()
+    enc.close()
+    assert stats["fc1"][1] == 3 * g.n_layers and stats["attention"][1] == 3 * g.n_layers
+    assert stats["layernorm"][1] == 3 * 2 * g.n_layers
+    assert all(ms >= 0 for ms, _ in stats.values())
+
+
+def test_forward_rejects_bad_arguments(aenc):
+    w = reduced("whisper_large_b1", "args", dict(n_layers=0, n_frames=64))
+    g = w.geom
+    W = synth.make_weights(w)
+    enc = aenc.Encoder(g, device_weights(W, g.dtype))
+    with pytest.raises(ValueError):
+        enc.forward(torch.zeros(1, g.n_mel, g.n_frames + 2, device=DEV, dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        enc.forward(torch.zeros(1, g.n_mel, g.n_frames, device=DEV, dtype=torch.float32))
+    st = aenc.lib().aenc_forward(enc._h, None, None, None, None)
+    assert st == -1 and "NULL" in aenc.last_error()
+    enc.close()
