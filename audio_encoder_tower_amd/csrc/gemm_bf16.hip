@@ -5,11 +5,22 @@
 // is row-major (the [out, in] checkpoint layout). K must be a multiple of 64.
 //
 // Tiling: a 256-thread workgroup (4 wave64s) owns a BM x BN tile of C; each
-// wave owns WM x WN and issues v_mfma_f32_32x32x16_bf16 on 32x32 sub-tiles.
-// K advances in slices of 64 staged through LDS with two buffers: the global
-// loads of slice k+1 are in flight while slice k feeds the matrix cores.
-// LDS rows are 128 bytes; 16-byte chunks are XOR-swizzled by (row mod 8) so
-// that the 128-bit fragment reads of eight consecutive rows hit distinct banks.
+// wave owns (BM/2) x (BN/2) and issues v_mfma_f32_32x32x16_bf16 on 32x32
+// sub-tiles, accumulating in the AGPR half of the register file.
+//
+// K advances in slices of 64 through two LDS buffers. Slices are copied
+// global -> LDS by global_load_lds_dwordx4 (gfx950): no staging registers
+// and no LDS write instructions, so the registers go to the accumulators and
+// to double-buffered MFMA fragments. The two buffers are distinct LDS objects
+// and the slice loop is unrolled by two, so the copy into one buffer never
+// forces a wait in front of the reads of the other.
+//
+// LDS rows are 128 bytes (64 bf16 of K); the 16-byte chunk c of row r is
+// stored at position c ^ (r mod 8), so the 128-bit fragment reads of eight
+// consecutive rows hit distinct banks. The direct-to-LDS copy writes 16 bytes
+// per lane at consecutive addresses, so each lane fetches the global chunk
+// that belongs at its LDS position.
+//
 // Workgroup ids are remapped so that each of the 8 XCDs (private L2 each)
 // works on a contiguous range of tiles, grouped GROUP_M tiles tall, so the A
 // and W panels those tiles share stay in that XCD's L2.
@@ -35,18 +46,84 @@ struct GemmArgs {
   EpiParams epi;
 };
 
-__device__ __forceinline__ int swz(int row, int chunk) { return (chunk ^ (row & 7)); }
+typedef __attribute__((address_space(3))) void lds_void;
+typedef const __attribute__((address_space(1))) void gbl_void;
 
-template <int BM, int BN, int WM, int WN, int EPI>
+// Per-lane element offsets (from the operand base) of the rows this lane
+// copies, one per copy instruction.
+template <int ROWS>
+struct CopyPlan {
+  int32_t off[ROWS / 32];
+};
+
+// Copy one 64-wide K slice of ROWS rows into an LDS tile: each wave issues
+// ROWS/32 instructions of 8 rows (64 lanes x 16 bytes).
+template <int ROWS>
+__device__ __forceinline__ void copy_slice(const bf16_t* base, const CopyPlan<ROWS>& plan, int k0, bf16_t* lds,
+                                           int wave) {
+#pragma unroll
+  for (int i = 0; i < ROWS / 32; ++i) {
+    const int row0 = (wave * (ROWS / 32) + i) * 8;
+    __builtin_amdgcn_global_load_lds((gbl_void*)(base + plan.off[i] + k0), (lds_void*)(lds + row0 * GEMM_BK), 16, 0,
+                                     0);
+  }
+}
+
+// vmcnt(0): every global -> LDS copy this wave issued has landed.
+__device__ __forceinline__ void wait_copies() { __builtin_amdgcn_s_waitcnt(0x3f70); }
+
+// Fragments of one 16-wide K step: rows (lane & 31) of each 32-row sub-tile,
+// K half (lane >> 5); the 16-byte chunk index is swizzled by (row mod 8).
+template <int S>
+__device__ __forceinline__ void read_frags(const bf16_t* base, int row0, int ch, bf16x8 (&f)[S]) {
+#pragma unroll
+  for (int i = 0; i < S; ++i) f[i] = *(const bf16x8*)(base + (row0 + 32 * i) * GEMM_BK + ch * 8);
+}
+
+template <int SM, int SN>
+__device__ __forceinline__ void mma(f32x16 (&acc)[SM][SN], const bf16x8 (&fa)[SM], const bf16x8 (&fb)[SN]) {
+#pragma unroll
+  for (int i = 0; i < SM; ++i)
+#pragma unroll
+    for (int j = 0; j < SN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+}
+
+// One 64-wide K slice from LDS tiles (as, bs): fragments of step s+1 are read
+// while step s multiplies.
+// The scheduler barriers pin this order, so the LDS reads of the next step are
+// in flight while the matrix cores work on the current one.
+template <int SM, int SN>
+__device__ __forceinline__ void slice(f32x16 (&acc)[SM][SN], const bf16_t* as, const bf16_t* bs, int a_row0,
+                                      int b_row0, int fr, int fk) {
+  bf16x8 fa0[SM], fb0[SN], fa1[SM], fb1[SN];
+  const int sw = fr & 7;
+  read_frags<SM>(as, a_row0, (0 + fk) ^ sw, fa0);
+  read_frags<SN>(bs, b_row0, (0 + fk) ^ sw, fb0);
+  read_frags<SM>(as, a_row0, (2 + fk) ^ sw, fa1);
+  read_frags<SN>(bs, b_row0, (2 + fk) ^ sw, fb1);
+  __builtin_amdgcn_sched_barrier(0);
+  mma<SM, SN>(acc, fa0, fb0);
+  __builtin_amdgcn_sched_barrier(0);
+  read_frags<SM>(as, a_row0, (4 + fk) ^ sw, fa0);
+  read_frags<SN>(bs, b_row0, (4 + fk) ^ sw, fb0);
+  __builtin_amdgcn_sched_barrier(0);
+  mma<SM, SN>(acc, fa1, fb1);
+  __builtin_amdgcn_sched_barrier(0);
+  read_frags<SM>(as, a_row0, (6 + fk) ^ sw, fa1);
+  read_frags<SN>(bs, b_row0, (6 + fk) ^ sw, fb1);
+  __builtin_amdgcn_sched_barrier(0);
+  mma<SM, SN>(acc, fa0, fb0);
+  __builtin_amdgcn_sched_barrier(0);
+  mma<SM, SN>(acc, fa1, fb1);
+}
+
+template <int BM, int BN, int EPI>
 __global__ __launch_bounds__(GEMM_THREADS) void gemm_bf16_kernel(GemmArgs g) {
-  constexpr int WAVES_N = BN / WN;
-  static_assert((BM / WM) * (BN / WN) == 4, "four waves per workgroup");
-  constexpr int SM = WM / 32, SN = WN / 32;        // 32x32 sub-tiles per wave
-  constexpr int A_LD = BM * 8 / GEMM_THREADS;       // 16-byte chunks per thread per slice
-  constexpr int B_LD = BN * 8 / GEMM_THREADS;
-  extern __shared__ __align__(16) unsigned char smem[];
-  bf16_t* As = (bf16_t*)smem;                       // [2][BM][64]
-  bf16_t* Bs = As + 2 * BM * GEMM_BK;               // [2][BN][64]
+  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int SM = WM / 32, SN = WN / 32;   // 32x32 sub-tiles per wave
+  // Two slice buffers, A rows then W rows, as distinct LDS objects.
+  __shared__ __attribute__((aligned(16))) bf16_t buf0[(BM + BN) * GEMM_BK];
+  __shared__ __attribute__((aligned(16))) bf16_t buf1[(BM + BN) * GEMM_BK];
 
   // ---- tile selection: XCD-contiguous ranges, then GROUP_M-tall groups ----
   const int total = g.tiles_m * g.tiles_n;
@@ -67,39 +144,24 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_bf16_kernel(GemmArgs g) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int wm = wave >> 1, wn = wave & 1;
 
-  // ---- global load pointers (each thread: fixed chunk column, rows tid/8 + 32 i) ----
-  const int ld_row = tid >> 3, ld_ch = tid & 7;
-  const bf16_t* a_src[A_LD];
-  const bf16_t* b_src[B_LD];
+  // ---- copy plans: lane l of an instruction covers row row0 + l/8 and LDS chunk
+  //      l%8, which holds the global chunk (l%8) ^ (row mod 8) ----
+  const int c_row = lane >> 3;
+  const int c_chunk = (lane & 7) ^ (c_row & 7);
+  CopyPlan<BM> pa;
+  CopyPlan<BN> pb;
 #pragma unroll
-  for (int i = 0; i < A_LD; ++i) {
-    const int r = min(m0 + ld_row + 32 * i, M - 1);
-    a_src[i] = g.A + g.arow.offset(r) + ld_ch * 8;
+  for (int i = 0; i < BM / 32; ++i) {
+    const int r = (wave * (BM / 32) + i) * 8 + c_row;
+    pa.off[i] = (int32_t)g.arow.offset(min(m0 + r, M - 1)) + c_chunk * 8;
   }
 #pragma unroll
-  for (int i = 0; i < B_LD; ++i) {
-    const int r = min(n0 + ld_row + 32 * i, g.N - 1);
-    b_src[i] = g.W + (int64_t)r * g.ldw + ld_ch * 8;
+  for (int i = 0; i < BN / 32; ++i) {
+    const int r = (wave * (BN / 32) + i) * 8 + c_row;
+    pb.off[i] = (int32_t)((int64_t)min(n0 + r, g.N - 1) * g.ldw) + c_chunk * 8;
   }
-  const int st_off = ld_row * GEMM_BK + swz(ld_row, ld_ch) * 8;  // + 32*64*i per chunk
-
-  u32x4 ra[A_LD], rb[B_LD];
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < A_LD; ++i) ra[i] = *(const u32x4*)(a_src[i] + k0);
-#pragma unroll
-    for (int i = 0; i < B_LD; ++i) rb[i] = *(const u32x4*)(b_src[i] + k0);
-  };
-  auto lstore = [&](int buf) {
-    bf16_t* a = As + buf * BM * GEMM_BK + st_off;
-    bf16_t* b = Bs + buf * BN * GEMM_BK + st_off;
-#pragma unroll
-    for (int i = 0; i < A_LD; ++i) *(u32x4*)(a + i * 32 * GEMM_BK) = ra[i];
-#pragma unroll
-    for (int i = 0; i < B_LD; ++i) *(u32x4*)(b + i * 32 * GEMM_BK) = rb[i];
-  };
 
   f32x16 acc[SM][SN];
 #pragma unroll
@@ -109,93 +171,93 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  // fragment rows of this lane
   const int fr = lane & 31, fk = lane >> 5;
   const int a_row0 = wm * WM + fr;
   const int b_row0 = wn * WN + fr;
+  bf16_t* const a0 = buf0;
+  bf16_t* const b0 = buf0 + BM * GEMM_BK;
+  bf16_t* const a1 = buf1;
+  bf16_t* const b1 = buf1 + BM * GEMM_BK;
 
   const int nk = g.K / GEMM_BK;
-  gload(0);
-  lstore(0);
+  copy_slice<BM>(g.A, pa, 0, a0, wave);
+  copy_slice<BN>(g.W, pb, 0, b0, wave);
+  wait_copies();
   __syncthreads();
 
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * GEMM_BK);
-    const bf16_t* a_lds = As + buf * BM * GEMM_BK;
-    const bf16_t* b_lds = Bs + buf * BN * GEMM_BK;
-#pragma unroll
-    for (int s = 0; s < GEMM_BK / 16; ++s) {
-      const int ch = 2 * s + fk;
-      bf16x8 af[SM], bfr[SN];
-#pragma unroll
-      for (int i = 0; i < SM; ++i) {
-        const int r = a_row0 + 32 * i;
-        af[i] = *(const bf16x8*)(a_lds + r * GEMM_BK + swz(r, ch) * 8);
-      }
-#pragma unroll
-      for (int j = 0; j < SN; ++j) {
-        const int r = b_row0 + 32 * j;
-        bfr[j] = *(const bf16x8*)(b_lds + r * GEMM_BK + swz(r, ch) * 8);
-      }
-#pragma unroll
-      for (int i = 0; i < SM; ++i)
-#pragma unroll
-        for (int j = 0; j < SN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    // slice kt from buffer 0 while slice kt+1 lands in buffer 1
+    copy_slice<BM>(g.A, pa, (kt + 1) * GEMM_BK, a1, wave);
+    copy_slice<BN>(g.W, pb, (kt + 1) * GEMM_BK, b1, wave);
+    __builtin_amdgcn_sched_barrier(0);   // keep the copies ahead of the slice
+    slice<SM, SN>(acc, a0, b0, a_row0, b_row0, fr, fk);
+    wait_copies();
+    __syncthreads();
+    // slice kt+1 from buffer 1 while slice kt+2 lands in buffer 0
+    if (kt + 2 < nk) {
+      copy_slice<BM>(g.A, pa, (kt + 2) * GEMM_BK, a0, wave);
+      copy_slice<BN>(g.W, pb, (kt + 2) * GEMM_BK, b0, wave);
     }
-    if (kt + 1 < nk) lstore(buf ^ 1);
+    __builtin_amdgcn_sched_barrier(0);
+    slice<SM, SN>(acc, a1, b1, a_row0, b_row0, fr, fk);
+    wait_copies();
+    __syncthreads();
+  }
+  if (kt < nk) {   // odd slice count: the last slice sits in buffer 0
+    slice<SM, SN>(acc, a0, b0, a_row0, b_row0, fr, fk);
     __syncthreads();
   }
 
-  // ---- epilogue: lane holds column (lane & 31); rows 8*(v/4) + 4*(lane>>5) + v%4 ----
+  // ---- epilogue through LDS: each wave stages 32-row slabs of its fp32 tile
+  //      (lane holds column lane&31 and rows 8*(v/4) + 4*(lane>>5) + v%4 of each
+  //      32x32 sub-tile), then writes them back row-contiguously ----
+  constexpr int LDW = WN + 4;                        // padded slab row, floats
+  float* slab = (float*)(wave < 2 ? buf0 : buf1) + (wave & 1) * (32 * LDW);
+  const int col0 = n0 + wn * WN;
 #pragma unroll
-  for (int i = 0; i < SM; ++i)
+  for (int i = 0; i < SM; ++i) {
 #pragma unroll
     for (int j = 0; j < SN; ++j)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int r0 = m0 + wm * WM + 32 * i + 8 * q + 4 * fk;
-        const int n = n0 + wn * WN + 32 * j + fr;
-        const f32x4 v = {acc[i][j][4 * q + 0], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                         acc[i][j][4 * q + 3]};
-        Epilogue<EPI>::apply4(g.epi, r0, n, v, M, g.N);
-      }
+      for (int v = 0; v < 16; ++v) slab[(8 * (v >> 2) + 4 * fk + (v & 3)) * LDW + 32 * j + fr] = acc[i][j][v];
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the slab is written
+    __builtin_amdgcn_wave_barrier();
+    Epilogue<EPI>::template slab32<WN, LDW>(g.epi, slab, m0 + wm * WM + 32 * i, col0, lane, M, g.N);
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // reads done before the next slab overwrites it
+    __builtin_amdgcn_wave_barrier();
+  }
 }
 
-template <int BM, int BN, int WM, int WN, int EPI>
+template <int BM, int BN, int EPI>
 static hipError_t launch_cfg(const GemmArgs& in, hipStream_t stream) {
   GemmArgs g = in;
   g.tiles_m = (g.M + BM - 1) / BM;
   g.tiles_n = (g.N + BN - 1) / BN;
   const int total = g.tiles_m * g.tiles_n;
   g.grid = (total + N_XCD - 1) / N_XCD * N_XCD;
-  const size_t lds = (size_t)2 * (BM + BN) * GEMM_BK * sizeof(bf16_t);
-  static bool attr_set = false;
-  if (!attr_set) {
-    // Raise the dynamic LDS limit of this instance above 64 KiB (gfx950 has 160 KiB).
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_bf16_kernel<BM, BN, WM, WN, EPI>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, EPI>), dim3(g.grid), dim3(GEMM_THREADS), lds, stream, g);
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, EPI>), dim3(g.grid), dim3(GEMM_THREADS), 0, stream, g);
   return hipGetLastError();
 }
 
 template <int EPI>
 static hipError_t launch_epi(const GemmArgs& g, int tile_cfg, hipStream_t stream) {
   switch (tile_cfg) {
-    case GEMM_TILE_256x256: return launch_cfg<256, 256, 128, 128, EPI>(g, stream);
-    case GEMM_TILE_256x128: return launch_cfg<256, 128, 128, 64, EPI>(g, stream);
-    case GEMM_TILE_128x128: return launch_cfg<128, 128, 64, 64, EPI>(g, stream);
+    case GEMM_TILE_256x256: return launch_cfg<256, 256, EPI>(g, stream);
+    case GEMM_TILE_256x128: return launch_cfg<256, 128, EPI>(g, stream);
+    case GEMM_TILE_128x128: return launch_cfg<128, 128, EPI>(g, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t gemm_bf16(int epi, const bf16_t* A, RowMap arow, const bf16_t* W, int64_t ldw, int M, int N, int K,
                      const int32_t* m_dev, const EpiParams& ep, int tile_cfg, hipStream_t stream) {
-  if (K % GEMM_BK != 0 || M <= 0 || N <= 0) return hipErrorInvalidValue;
+  // K in whole slices; N in groups of 4 (the epilogue writes 4 columns per lane).
+  if (K % GEMM_BK != 0 || M <= 0 || N <= 0 || N % 4 != 0) return hipErrorInvalidValue;
+  // V columns of the QKV epilogue start on a wave boundary.
+  if (epi == EPI_QKV_BF16 && ep.n_split % 128 != 0) return hipErrorInvalidValue;
+  // The copy plans hold 32-bit element offsets.
+  if ((int64_t)N * ldw >= INT32_MAX) return hipErrorInvalidValue;
   GemmArgs g{};
   g.A = A; g.arow = arow; g.W = W; g.ldw = ldw; g.M = M; g.N = N; g.K = K; g.m_dev = m_dev; g.epi = ep;
   switch (epi) {

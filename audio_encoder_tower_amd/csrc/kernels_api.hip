@@ -30,7 +30,8 @@ int hip_status(hipError_t e, const char* what) {
 extern "C" int aenc_k_gemm_bf16(int epi, const void* A, int64_t lda, const void* W, const float* bias, void* C,
                                 int64_t ldc, int M, int N, int K, int tile, void* stream) {
   if (!A || !W || !C) return fail("NULL operand");
-  if (M < 1 || N < 1 || K < 64 || K % 64 || lda < K || lda % 8 || ldc < N) return fail("bad GEMM sizes");
+  if (M < 1 || N < 1 || N % 4 || K < 64 || K % 64 || lda < K || lda % 8 || ldc < N || ldc % 4)
+    return fail("bad GEMM sizes (need N % 4 == 0, K % 64 == 0, lda % 8 == 0, ldc % 4 == 0)");
   int kind;
   switch (epi) {
     case AENC_EPI_BF16: kind = EPI_STORE_BF16; break;

@@ -34,6 +34,8 @@ def gemm_bf16(epi: str, a: torch.Tensor, w: torch.Tensor, bias: Optional[torch.T
     N = w.shape[0]
     assert a.dtype == w.dtype == torch.bfloat16 and w.shape[1] == K and c.shape == (M, N)
     assert bias is None or (bias.dtype == torch.float32 and bias.numel() == N)
+    want = torch.bfloat16 if epi in ("bf16", "gelu_bf16") else torch.float32
+    assert c.dtype == want, f"epilogue {epi} writes {want}, got a {c.dtype} output"
     check(lib().aenc_k_gemm_bf16(EPI[epi], _p(a), K, _p(w), _p(bias), _p(c), N, M, N, K, TILE[tile], _s()),
           "aenc_k_gemm_bf16")
     return c
@@ -60,6 +62,7 @@ def attention_bf16(qk: torch.Tensor, vt: torch.Tensor, start: torch.Tensor, lens
 def layernorm(x: torch.Tensor, gamma: torch.Tensor, beta: torch.Tensor, y: torch.Tensor, eps: float) -> torch.Tensor:
     M, d = x.shape
     assert x.dtype == gamma.dtype == beta.dtype == torch.float32 and y.shape == (M, d)
+    assert y.dtype in (torch.float32, torch.bfloat16)
     y_code = 1 if y.dtype == torch.bfloat16 else 0
     check(lib().aenc_k_layernorm(_p(x), _p(gamma), _p(beta), _p(y), y_code, M, d, eps, _s()), "aenc_k_layernorm")
     return y

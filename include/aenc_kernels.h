@@ -35,8 +35,8 @@ enum { AENC_TILE_256x256 = 0, AENC_TILE_256x128 = 1, AENC_TILE_128x128 = 2 };
 
 /* C[M, N] = epi(A[M, K] W[N, K]^T + bias[N]) with bf16 A and W (row-major,
  * leading dimensions lda, K and ldc in elements), fp32 accumulate.
- * bias: fp32 [N] or NULL. K must be a positive multiple of 64; lda a multiple
- * of 8; M, N >= 1. */
+ * bias: fp32 [N] or NULL, 16-byte aligned. K must be a positive multiple of
+ * 64; N a positive multiple of 4; lda a multiple of 8 and ldc of 4; M >= 1. */
 int aenc_k_gemm_bf16(int epi, const void *A, int64_t lda, const void *W, const float *bias, void *C,
                      int64_t ldc, int M, int N, int K, int tile, void *stream);
 

@@ -63,7 +63,7 @@ def test_gemm_bf16(_lib, shape, epi, tile):
         ref = ref + c_in
         c = dev_f32(c_in)
     elif epi == "f32":
-        c = torch.full((M, N), float("nan"), device=DEV)
+        c = torch.full((M, N), float("nan"), device=DEV, dtype=torch.float32)
     else:
         c = torch.full((M, N), float("nan"), device=DEV, dtype=torch.bfloat16)
     if epi == "gelu_bf16":
@@ -98,7 +98,7 @@ def test_qkv_split_layout(_lib):
 
 def test_gelu_device_erf(_lib):
     x = np.concatenate([np.linspace(-12, 12, 200001), [0.0, -0.0, 1e-30, -1e-30, 40.0, -40.0]]).astype(np.float32)
-    y = torch.empty(x.size, device=DEV)
+    y = torch.empty(x.size, device=DEV, dtype=torch.float32)
     _lib.steps.gelu_f32(dev_f32(x), y)
     torch.cuda.synchronize()
     ref = oracle.gelu(x.astype(np.float64))

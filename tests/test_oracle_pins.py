@@ -15,7 +15,15 @@ import oracle
 import synth
 from oracle import encoder as E
 
-torch.set_default_dtype(torch.float64)
+
+
+@pytest.fixture(autouse=True)
+def _float64_modules():
+    """torch.nn modules built by these tests hold float64 parameters."""
+    old = torch.get_default_dtype()
+    torch.set_default_dtype(torch.float64)
+    yield
+    torch.set_default_dtype(old)
 
 
 def tiny_workload(**geom_kw):

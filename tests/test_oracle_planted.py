@@ -12,7 +12,7 @@ import pytest
 import oracle
 import synth
 from oracle import encoder as E
-from tests.test_oracle_pins import TOWER_CASES, tiny_workload, torch_encoder
+from tests.test_oracle_pins import TOWER_CASES, _float64_modules, tiny_workload, torch_encoder  # noqa: F401
 
 
 def _tower_pins_pass() -> bool:
