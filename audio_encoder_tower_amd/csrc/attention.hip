@@ -27,7 +27,10 @@ constexpr int ATT_BQ = 128;
 constexpr int ATT_BK = 64;
 constexpr int ATT_D = 64;
 
-__device__ __forceinline__ int att_swz(int row, int chunk) { return chunk ^ (row & 7); }
+// LDS tiles have 128-byte rows; a 128-bit read is served for 16 lanes per
+// cycle from 64 banks (two rows), so chunk c of row r sits at c ^ ((r/2) mod 8)
+// and 16 consecutive rows reading the same chunk use 16 distinct bank groups.
+__device__ __forceinline__ int att_swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
 
 __global__ __launch_bounds__(256) void attention_bf16_kernel(const bf16_t* __restrict__ qk, int64_t ld_qk,
                                                              const bf16_t* __restrict__ vt, int64_t ld_vt,

@@ -15,11 +15,13 @@
 // and the slice loop is unrolled by two, so the copy into one buffer never
 // forces a wait in front of the reads of the other.
 //
-// LDS rows are 128 bytes (64 bf16 of K); the 16-byte chunk c of row r is
-// stored at position c ^ (r mod 8), so the 128-bit fragment reads of eight
-// consecutive rows hit distinct banks. The direct-to-LDS copy writes 16 bytes
-// per lane at consecutive addresses, so each lane fetches the global chunk
-// that belongs at its LDS position.
+// LDS rows are 128 bytes (64 bf16 of K). The LDS serves a 128-bit read for 16
+// lanes per cycle from 64 four-byte banks, i.e. two rows' worth of banks, so
+// the 16-byte chunk c of row r is stored at position c ^ ((r / 2) mod 8):
+// sixteen consecutive rows reading the same chunk then hit 16 distinct bank
+// groups. The direct-to-LDS copy writes 16 bytes per lane at consecutive
+// addresses, so each lane fetches the global chunk that belongs at its LDS
+// position.
 //
 // Workgroup ids are remapped so that each of the 8 XCDs (private L2 each)
 // works on a contiguous range of tiles, grouped GROUP_M tiles tall, so the A
@@ -73,7 +75,7 @@ __device__ __forceinline__ void copy_slice(const bf16_t* base, const CopyPlan<RO
 __device__ __forceinline__ void wait_copies() { __builtin_amdgcn_s_waitcnt(0x3f70); }
 
 // Fragments of one 16-wide K step: rows (lane & 31) of each 32-row sub-tile,
-// K half (lane >> 5); the 16-byte chunk index is swizzled by (row mod 8).
+// K half (lane >> 5); the 16-byte chunk index is swizzled by (row / 2) mod 8.
 template <int S>
 __device__ __forceinline__ void read_frags(const bf16_t* base, int row0, int ch, bf16x8 (&f)[S]) {
 #pragma unroll
@@ -96,7 +98,7 @@ template <int SM, int SN>
 __device__ __forceinline__ void slice(f32x16 (&acc)[SM][SN], const bf16_t* as, const bf16_t* bs, int a_row0,
                                       int b_row0, int fr, int fk) {
   bf16x8 fa0[SM], fb0[SN], fa1[SM], fb1[SN];
-  const int sw = fr & 7;
+  const int sw = (fr >> 1) & 7;   // sub-tile rows start on multiples of 16
   read_frags<SM>(as, a_row0, (0 + fk) ^ sw, fa0);
   read_frags<SN>(bs, b_row0, (0 + fk) ^ sw, fb0);
   read_frags<SM>(as, a_row0, (2 + fk) ^ sw, fa1);
@@ -146,21 +148,25 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_bf16_kernel(GemmArgs g) {
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
-  // ---- copy plans: lane l of an instruction covers row row0 + l/8 and LDS chunk
-  //      l%8, which holds the global chunk (l%8) ^ (row mod 8) ----
+  // ---- copy plans: lane l of an instruction covers row row0 + l/8 (row0 a
+  //      multiple of 8) and LDS chunk l%8, which holds the global chunk
+  //      (l%8) ^ ((row / 2) mod 8) ----
   const int c_row = lane >> 3;
-  const int c_chunk = (lane & 7) ^ (c_row & 7);
+  const int c_chunk_lo = (lane & 7) ^ (c_row >> 1);        // rows with (row0/2) % 8 == 0
+  const int c_chunk_hi = (lane & 7) ^ ((c_row >> 1) + 4);  // rows with (row0/2) % 8 == 4
   CopyPlan<BM> pa;
   CopyPlan<BN> pb;
 #pragma unroll
   for (int i = 0; i < BM / 32; ++i) {
-    const int r = (wave * (BM / 32) + i) * 8 + c_row;
-    pa.off[i] = (int32_t)g.arow.offset(min(m0 + r, M - 1)) + c_chunk * 8;
+    const int row0 = (wave * (BM / 32) + i) * 8;
+    const int r = row0 + c_row;
+    pa.off[i] = (int32_t)g.arow.offset(min(m0 + r, M - 1)) + ((row0 & 8) ? c_chunk_hi : c_chunk_lo) * 8;
   }
 #pragma unroll
   for (int i = 0; i < BN / 32; ++i) {
-    const int r = (wave * (BN / 32) + i) * 8 + c_row;
-    pb.off[i] = (int32_t)((int64_t)min(n0 + r, g.N - 1) * g.ldw) + c_chunk * 8;
+    const int row0 = (wave * (BN / 32) + i) * 8;
+    const int r = row0 + c_row;
+    pb.off[i] = (int32_t)((int64_t)min(n0 + r, g.N - 1) * g.ldw) + ((row0 & 8) ? c_chunk_hi : c_chunk_lo) * 8;
   }
 
   f32x16 acc[SM][SN];
@@ -212,7 +218,9 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_bf16_kernel(GemmArgs g) {
   // ---- epilogue through LDS: each wave stages 32-row slabs of its fp32 tile
   //      (lane holds column lane&31 and rows 8*(v/4) + 4*(lane>>5) + v%4 of each
   //      32x32 sub-tile), then writes them back row-contiguously ----
-  constexpr int LDW = WN + 4;                        // padded slab row, floats
+  // Slab rows padded to WN + 8 floats: lanes 32-63 write 4 rows below lanes
+  // 0-31, which then lands on the other half of the 64 banks.
+  constexpr int LDW = WN + 8;
   float* slab = (float*)(wave < 2 ? buf0 : buf1) + (wave & 1) * (32 * LDW);
   const int col0 = n0 + wn * WN;
 #pragma unroll
