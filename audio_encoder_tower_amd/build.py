@@ -40,11 +40,16 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
+# Per-source extra device flags. The attention kernel's softmax works on the
+# MFMA results directly, so they are kept in VGPRs rather than the AGPR file.
+SOURCE_FLAGS = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def compile_one(src: str, debug: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-std=c++17", "-fPIC", "-c", src, "-o", obj,
            "-O1" if debug else "-O3", "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include")]
-    cmd += DEVICE_FLAGS
+    cmd += DEVICE_FLAGS + SOURCE_FLAGS.get(os.path.basename(src), [])
     res = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass does not know the device feature flag above and says so.
     noise = "'-packed-fp32-ops' is not a recognized feature for this target"

@@ -18,6 +18,8 @@
 //     goes through LDS; V^T's keys are stored in the order that matches;
 //   - scores are scaled by 1/sqrt(64) and turned into base-2 exponents in a
 //     single fma; softmax statistics and the output accumulate in fp32.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -62,16 +64,21 @@ __global__ __launch_bounds__(256) void attention_bf16_kernel(const bf16_t* __res
   const bf16_t* kbase = qk + d + h * ATT_D;
   const bf16_t* vbase = vt + (int64_t)(h * ATT_D) * ld_vt + start;
   u32x4 rk[2], rv[2];
-  auto gload = [&](int k0) {
+  // RAGGED: the tile may run past the clip; key rows are clamped and the
+  // values of keys past the clip are zeroed (a zero probability times a
+  // non-finite value would still poison the sum).
+  auto gload = [&](int k0, auto ragged) {
+    constexpr bool RAGGED = decltype(ragged)::value;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int c = tid + 256 * i;
       const int key = c >> 3, ch = c & 7;
-      rk[i] = *(const u32x4*)(kbase + (int64_t)(start + min(k0 + key, len - 1)) * ld_qk + ch * 8);
+      const int krow = RAGGED ? min(k0 + key, len - 1) : k0 + key;
+      rk[i] = *(const u32x4*)(kbase + (int64_t)(start + krow) * ld_qk + ch * 8);
       const int e = c >> 3, kc = c & 7;
       u32x4 v = *(const u32x4*)(vbase + (int64_t)e * ld_vt + k0 + kc * 8);
-      const int first = k0 + kc * 8;
-      if (first + 8 > len) {            // ragged end: zero the values of keys past the clip
+      if (RAGGED) {
+        const int first = k0 + kc * 8;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           uint32_t word = v[w];
@@ -110,16 +117,9 @@ __global__ __launch_bounds__(256) void attention_bf16_kernel(const bf16_t* __res
 #pragma unroll
     for (int v = 0; v < 16; ++v) oacc[es][v] = 0.0f;
 
-  const int n_tiles = (len + ATT_BK - 1) / ATT_BK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-
-  for (int kt = 0; kt < n_tiles; ++kt) {
-    const int buf = kt & 1;
-    const int k0 = kt * ATT_BK;
-    if (kt + 1 < n_tiles) gload(k0 + ATT_BK);
-
+  // One 64-key tile from LDS buffer `buf`; RAGGED: keys past the clip are masked.
+  auto tile = [&](int buf, int k0, auto ragged) {
+    constexpr bool RAGGED = decltype(ragged)::value;
     // ---- S^T = K Q^T for two 32-key sub-tiles ----
     f32x16 s[2];
 #pragma unroll
@@ -134,14 +134,13 @@ __global__ __launch_bounds__(256) void attention_bf16_kernel(const bf16_t* __res
       }
     }
     // lane holds keys 32 sub + 8 (v >> 2) + 4 hh + (v & 3) of query qi
-    if (k0 + ATT_BK > len) {
+    if (RAGGED) {
+      const int nvalid = len - k0 - 4 * hh;
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int key = k0 + 32 * sub + 8 * (v >> 2) + 4 * hh + (v & 3);
-          if (key >= len) s[sub][v] = -INFINITY;
-        }
+        for (int v = 0; v < 16; ++v)
+          if (32 * sub + 8 * (v >> 2) + (v & 3) >= nvalid) s[sub][v] = -INFINITY;
     }
     float mx = s[0][0];
 #pragma unroll
@@ -149,10 +148,19 @@ __global__ __launch_bounds__(256) void attention_bf16_kernel(const bf16_t* __res
 #pragma unroll
       for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[sub][v]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
-    const float mc = m_new * c;
-    m_run = m_new;
+    // Rescale the running sums only when some row's maximum grew (a uniform
+    // branch: after the first tiles the maximum rarely moves).
+    if (__any(mx > m_run)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int es = 0; es < 2; ++es)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) oacc[es][v] *= alpha;
+    }
+    const float mc = m_run * c;
 
     float lsum = 0.0f;
     bf16x8 pb[2][2];
@@ -166,11 +174,7 @@ __global__ __launch_bounds__(256) void attention_bf16_kernel(const bf16_t* __res
           lsum += p;
           pb[sub][u][j] = (__bf16)p;
         }
-    l_run = l_run * alpha + lsum;
-#pragma unroll
-    for (int es = 0; es < 2; ++es)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) oacc[es][v] *= alpha;
+    l_run += lsum;
 
     // ---- O^T += V^T P^T ----
 #pragma unroll
@@ -184,10 +188,25 @@ __global__ __launch_bounds__(256) void attention_bf16_kernel(const bf16_t* __res
           oacc[es] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[sub][u], oacc[es], 0, 0, 0);
         }
     }
+  };
 
-    if (kt + 1 < n_tiles) lstore(buf ^ 1);
+  const int n_tiles = (len + ATT_BK - 1) / ATT_BK;
+  if (n_tiles == 1) gload(0, std::true_type{});
+  else gload(0, std::false_type{});
+  lstore(0);
+  __syncthreads();
+  // full tiles: prefetch the next tile into registers while this one computes
+  for (int kt = 0; kt + 1 < n_tiles; ++kt) {
+    const int buf = kt & 1;
+    const int k0 = kt * ATT_BK;
+    if (kt + 2 == n_tiles) gload(k0 + ATT_BK, std::true_type{});
+    else gload(k0 + ATT_BK, std::false_type{});
+    tile(buf, k0, std::false_type{});
+    lstore(buf ^ 1);
     __syncthreads();
   }
+  // the last tile may be ragged
+  tile((n_tiles - 1) & 1, (n_tiles - 1) * ATT_BK, std::true_type{});
 
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = 1.0f / l_tot;
