@@ -50,12 +50,14 @@ def attention_flops(g, tb) -> float:
     return float(sum(4.0 * t * t * g.d_model for t in tb))
 
 
-def cpu_baseline(w, blocks: int = 4):
-    """Time the oracle (as it is) on one clip: the stem, `blocks` of the blocks,
-    and the final norm (+ projector); block time is scaled to the full depth."""
+def cpu_baseline(w, blocks: int = 0):
+    """Time the oracle (as it is) on one clip: the stem, `blocks` of the blocks
+    (0: all of them) and the final norm (+ projector); block time is scaled to
+    the full depth when fewer blocks run."""
     import oracle
     from oracle import encoder as E
     g = w.geom
+    blocks = g.n_layers if blocks <= 0 else min(blocks, g.n_layers)
     W = synth.make_weights(w.replace(geom=g.replace(n_layers=blocks)))
     Wfull_proj = W
     mel = synth.make_mel(w, clips=[0])[0]
@@ -77,10 +79,43 @@ def cpu_baseline(w, blocks: int = 4):
         "cores": cores,
         "kind": "oracle",
         "sample": (f"1 clip of {w.name}: stem + {blocks} of {g.n_layers} blocks + final norm"
-                   f"{' + projector' if g.proj_hidden else ''}, fp64 NumPy; block time scaled x{g.n_layers / blocks:g}; "
+                   f"{' + projector' if g.proj_hidden else ''}, fp64 NumPy"
+                   f"{'' if blocks == g.n_layers else f'; block time scaled x{g.n_layers / blocks:g}'}; "
                    f"measured {t3 - t0:.1f} s"),
         "seconds_per_clip": round(per_clip, 3),
     }
+
+
+# Kernel sources whose change invalidates stored hardware-counter readings.
+KERNEL_SOURCES = {
+    kind: ["gemm_bf16.hip", "epilogue.h", "common.h", "runtime.hip"]
+    for kind in ("qkv", "o_proj", "fc1", "fc2", "proj1", "proj2")
+}
+KERNEL_SOURCES["attention"] = ["attention.hip", "common.h", "runtime.hip"]
+
+
+def source_digest(kind: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES.get(kind, []):
+        with open(os.path.join(ROOT, "audio_encoder_tower_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kind: str):
+    """HBM bytes per launch of `kind` from profiles/traffic.json (rocprofv3
+    FETCH_SIZE and WRITE_SIZE, scaled by the plain copy kernel's reading), or
+    None when absent or taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    entry = data.get("kernels", {}).get(kind)
+    if not entry or entry.get("source_digest") != source_digest(kind):
+        return None
+    return entry.get("bytes_per_launch")
 
 
 def main():
@@ -90,7 +125,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=synth.workloads.HEADLINE)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-blocks", type=int, default=4)
+    ap.add_argument("--cpu-blocks", type=int, default=0, help="blocks the CPU oracle runs (0: all)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="first run the plain copy kernel over this many MiB (a reference for traffic counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -122,6 +159,13 @@ def main():
     import oracle  # closed-form FLOP count only
     flops = oracle.flops(g, frames)
 
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        aenc.steps.copy(dst, src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         enc.forward(mel, mask, out, stream)
     torch.cuda.synchronize()
@@ -156,6 +200,9 @@ def main():
         fl = step_flops(g, k, rows) if k != "attention" else attention_flops(g, tb)
         if fl:
             entry["tflops"] = round(fl / (avg * 1e-3) / 1e12, 1)
+        if k == "layernorm":   # fp32 rows in, bf16 (or fp32) rows out
+            nbytes = rows * g.d_model * (4 + (2 if g.dtype == "bf16" else 4))
+            entry["gbs"] = round(nbytes / (avg * 1e-3) / 1e9, 1)
         per_kind[k] = entry
     dominant = max(kinds, key=lambda k: kinds[k][0])
     dom_ms, dom_n = kinds[dominant]
@@ -169,7 +216,7 @@ def main():
         "peak": peak,
         "unit": "TFLOP/s",
         "frac": round(dom_flops / (dom_avg * 1e-3) / 1e12 / peak, 4),
-        "traffic": None,
+        "traffic": measured_traffic(dominant),
         "avg_launch_ms": round(dom_avg, 5),
         "flops_per_launch": dom_flops,
     }
