@@ -90,13 +90,14 @@ __device__ __forceinline__ void mma(f32x16 (&acc)[SM][SN], const bf16x8 (&fa)[SM
     for (int j = 0; j < SN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
 }
 
-// One 64-wide K slice from LDS tiles (as, bs): fragments of step s+1 are read
-// while step s multiplies.
-// The scheduler barriers pin this order, so the LDS reads of the next step are
-// in flight while the matrix cores work on the current one.
-template <int SM, int SN>
+// One 64-wide K slice from LDS tiles (as, bs). Fragments of step s+1 are read
+// while step s multiplies; the copies of the next slice (if any) are spread
+// over the four steps instead of issued in one burst; the MFMA bursts run at
+// raised wave priority so that, with two workgroups per CU, the SIMD's other
+// wave does its memory work in the gaps. Scheduler barriers pin this order.
+template <int SM, int SN, class Copy>
 __device__ __forceinline__ void slice(f32x16 (&acc)[SM][SN], const bf16_t* as, const bf16_t* bs, int a_row0,
-                                      int b_row0, int fr, int fk) {
+                                      int b_row0, int fr, int fk, Copy&& copy_part) {
   bf16x8 fa0[SM], fb0[SN], fa1[SM], fb1[SN];
   const int sw = (fr >> 1) & 7;   // sub-tile rows start on multiples of 16
   read_frags<SM>(as, a_row0, (0 + fk) ^ sw, fa0);
@@ -104,20 +105,66 @@ __device__ __forceinline__ void slice(f32x16 (&acc)[SM][SN], const bf16_t* as, c
   read_frags<SM>(as, a_row0, (2 + fk) ^ sw, fa1);
   read_frags<SN>(bs, b_row0, (2 + fk) ^ sw, fb1);
   __builtin_amdgcn_sched_barrier(0);
+  copy_part(0);
+  __builtin_amdgcn_s_setprio(1);
   mma<SM, SN>(acc, fa0, fb0);
+  __builtin_amdgcn_s_setprio(0);
   __builtin_amdgcn_sched_barrier(0);
   read_frags<SM>(as, a_row0, (4 + fk) ^ sw, fa0);
   read_frags<SN>(bs, b_row0, (4 + fk) ^ sw, fb0);
+  copy_part(1);
   __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(1);
   mma<SM, SN>(acc, fa1, fb1);
+  __builtin_amdgcn_s_setprio(0);
   __builtin_amdgcn_sched_barrier(0);
   read_frags<SM>(as, a_row0, (6 + fk) ^ sw, fa1);
   read_frags<SN>(bs, b_row0, (6 + fk) ^ sw, fb1);
+  copy_part(2);
   __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(1);
   mma<SM, SN>(acc, fa0, fb0);
+  __builtin_amdgcn_s_setprio(0);
   __builtin_amdgcn_sched_barrier(0);
+  copy_part(3);
+  __builtin_amdgcn_s_setprio(1);
   mma<SM, SN>(acc, fa1, fb1);
+  __builtin_amdgcn_s_setprio(0);
 }
+
+// Part q (0..3) of the copy of one K slice: a quarter of this wave's copy
+// instructions (A rows first, then W rows).
+template <int BM, int BN>
+struct SliceCopy {
+  const bf16_t* A;
+  const bf16_t* W;
+  const CopyPlan<BM>* pa;
+  const CopyPlan<BN>* pb;
+  int k0;
+  bf16_t* la;
+  bf16_t* lb;
+  int wave;
+  bool live;   // uniform: false when there is no next slice
+  __device__ __forceinline__ void operator()(int q) const {
+    constexpr int NA = BM / 32, NB = BN / 32, N = NA + NB, PER = N / 4;
+    static_assert(N % 4 == 0, "copy instructions split into four parts");
+    if (!live) return;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int c = q * PER + j;
+      if (c < NA) {
+        const int row0 = (wave * NA + c) * 8;
+        __builtin_amdgcn_global_load_lds((gbl_void*)(A + pa->off[c] + k0), (lds_void*)(la + row0 * GEMM_BK), 16,
+                                         0, 0);
+      } else {
+        const int cb = c - NA;
+        const int row0 = (wave * NB + cb) * 8;
+        __builtin_amdgcn_global_load_lds((gbl_void*)(W + pb->off[cb] + k0), (lds_void*)(lb + row0 * GEMM_BK), 16,
+                                         0, 0);
+      }
+    }
+  }
+};
 
 template <int BM, int BN, int EPI>
 __global__ __launch_bounds__(GEMM_THREADS) void gemm_bf16_kernel(GemmArgs g) {
@@ -194,24 +241,19 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_bf16_kernel(GemmArgs g) {
   int kt = 0;
   for (; kt + 1 < nk; kt += 2) {
     // slice kt from buffer 0 while slice kt+1 lands in buffer 1
-    copy_slice<BM>(g.A, pa, (kt + 1) * GEMM_BK, a1, wave);
-    copy_slice<BN>(g.W, pb, (kt + 1) * GEMM_BK, b1, wave);
-    __builtin_amdgcn_sched_barrier(0);   // keep the copies ahead of the slice
-    slice<SM, SN>(acc, a0, b0, a_row0, b_row0, fr, fk);
+    slice<SM, SN>(acc, a0, b0, a_row0, b_row0, fr, fk,
+                  SliceCopy<BM, BN>{g.A, g.W, &pa, &pb, (kt + 1) * GEMM_BK, a1, b1, wave, true});
     wait_copies();
     __syncthreads();
-    // slice kt+1 from buffer 1 while slice kt+2 lands in buffer 0
-    if (kt + 2 < nk) {
-      copy_slice<BM>(g.A, pa, (kt + 2) * GEMM_BK, a0, wave);
-      copy_slice<BN>(g.W, pb, (kt + 2) * GEMM_BK, b0, wave);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    slice<SM, SN>(acc, a1, b1, a_row0, b_row0, fr, fk);
+    // slice kt+1 from buffer 1 while slice kt+2 (if any) lands in buffer 0
+    slice<SM, SN>(acc, a1, b1, a_row0, b_row0, fr, fk,
+                  SliceCopy<BM, BN>{g.A, g.W, &pa, &pb, (kt + 2) * GEMM_BK, a0, b0, wave, kt + 2 < nk});
     wait_copies();
     __syncthreads();
   }
   if (kt < nk) {   // odd slice count: the last slice sits in buffer 0
-    slice<SM, SN>(acc, a0, b0, a_row0, b_row0, fr, fk);
+    slice<SM, SN>(acc, a0, b0, a_row0, b_row0, fr, fk,
+                  SliceCopy<BM, BN>{g.A, g.W, &pa, &pb, 0, a1, b1, wave, false});
     __syncthreads();
   }
 
