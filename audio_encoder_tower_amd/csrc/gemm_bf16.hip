@@ -3,17 +3,15 @@
 // A [M, K] rows come through a RowMap (dense rows, or the overlapping
 // strided rows that turn the k=3 convolutions into implicit GEMMs); W [N, K]
 // is row-major (the [out, in] checkpoint layout). K must be a multiple of 64.
-//
-// Tiling: a 256-thread workgroup (4 wave64s) owns a BM x BN tile of C; each
-// wave owns (BM/2) x (BN/2) and issues v_mfma_f32_32x32x16_bf16 on 32x32
-// sub-tiles, accumulating in the AGPR half of the register file.
+// Every wave issues v_mfma_f32_32x32x16_bf16 on 32x32 sub-tiles of C.
 //
 // K advances in slices of 64 through two LDS buffers. Slices are copied
-// global -> LDS by global_load_lds_dwordx4 (gfx950): no staging registers
-// and no LDS write instructions, so the registers go to the accumulators and
-// to double-buffered MFMA fragments. The two buffers are distinct LDS objects
-// and the slice loop is unrolled by two, so the copy into one buffer never
-// forces a wait in front of the reads of the other.
+// global -> LDS by buffer_load_dwordx4 ... lds (direct to LDS, gfx950): no
+// staging registers and no LDS write instructions, and the slice's K offset
+// rides in the scalar offset, so a copy instruction needs no per-lane address
+// arithmetic. The buffers are distinct LDS objects and the slice loop is
+// unrolled by two, so the copy into one buffer never forces a wait in front
+// of the reads of the other.
 //
 // LDS rows are 128 bytes (64 bf16 of K). The LDS serves a 128-bit read for 16
 // lanes per cycle from 64 four-byte banks, i.e. two rows' worth of banks, so
@@ -22,6 +20,17 @@
 // groups. The direct-to-LDS copy writes 16 bytes per lane at consecutive
 // addresses, so each lane fetches the global chunk that belongs at its LDS
 // position.
+//
+// Two tile shapes:
+//  * 256x256, 8 waves (two per SIMD), each wave 64x128. The waves form two
+//    groups that alternate roles every phase (ping-pong): while one group's
+//    waves run a burst of 16 MFMAs at raised priority, the other group's
+//    waves, on the same SIMDs, read their next fragments from LDS and issue
+//    the copies of the next slice; a workgroup barrier ends each phase. One
+//    workgroup per CU (128 KiB of LDS). Used for the large GEMMs.
+//  * 128x128, 4 waves, each wave 64x64, two workgroups per CU that overlap
+//    each other's copies and MFMAs. Used when the 256x256 tiles would leave
+//    most CUs idle (short batches).
 //
 // Workgroup ids are remapped so that each of the 8 XCDs (private L2 each)
 // works on a contiguous range of tiles, grouped GROUP_M tiles tall, so the A
@@ -33,7 +42,6 @@
 namespace aenc {
 
 constexpr int GEMM_BK = 64;
-constexpr int GEMM_THREADS = 256;
 constexpr int GEMM_GROUP_M = 8;
 constexpr int N_XCD = 8;
 
@@ -44,38 +52,43 @@ struct GemmArgs {
   int64_t ldw;
   int M, N, K;
   const int32_t* m_dev;  // if set, M = *m_dev (rows beyond it are not computed)
+  uint32_t a_bytes, w_bytes;   // extents of A and W reachable through the row maps
   int tiles_m, tiles_n, grid;
   EpiParams epi;
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
-typedef const __attribute__((address_space(1))) void gbl_void;
 
-// Per-lane element offsets (from the operand base) of the rows this lane
-// copies, one per copy instruction.
-template <int ROWS>
-struct CopyPlan {
-  int32_t off[ROWS / 32];
-};
-
-// Copy one 64-wide K slice of ROWS rows into an LDS tile: each wave issues
-// ROWS/32 instructions of 8 rows (64 lanes x 16 bytes).
-template <int ROWS>
-__device__ __forceinline__ void copy_slice(const bf16_t* base, const CopyPlan<ROWS>& plan, int k0, bf16_t* lds,
-                                           int wave) {
-#pragma unroll
-  for (int i = 0; i < ROWS / 32; ++i) {
-    const int row0 = (wave * (ROWS / 32) + i) * 8;
-    __builtin_amdgcn_global_load_lds((gbl_void*)(base + plan.off[i] + k0), (lds_void*)(lds + row0 * GEMM_BK), 16, 0,
-                                     0);
-  }
+// Buffer resource over [base, base + bytes): raw addressing, 32-bit offsets.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// vmcnt(0): every global -> LDS copy this wave issued has landed.
+// One direct-to-LDS copy: lane l moves 16 bytes from byte voff + soff of the
+// buffer to LDS address lds + 16 l.
+__device__ __forceinline__ void copy16(__amdgpu_buffer_rsrc_t r, bf16_t* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, soff, 0, 0);
+}
+
+// vmcnt(0): every copy this wave issued has landed.
 __device__ __forceinline__ void wait_copies() { __builtin_amdgcn_s_waitcnt(0x3f70); }
+// lgkmcnt(0): every LDS read this wave issued has returned.
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xc07f); }
+
+// Workgroup barrier without the memory fences of __syncthreads (which would
+// also wait for the copies in flight); the empty asm statements keep the
+// compiler from moving memory accesses across it.
+#define AENC_BARRIER()                   \
+  do {                                   \
+    __builtin_amdgcn_sched_barrier(0);   \
+    asm volatile("" ::: "memory");       \
+    __builtin_amdgcn_s_barrier();        \
+    asm volatile("" ::: "memory");       \
+    __builtin_amdgcn_sched_barrier(0);   \
+  } while (0)
 
 // Fragments of one 16-wide K step: rows (lane & 31) of each 32-row sub-tile,
-// K half (lane >> 5); the 16-byte chunk index is swizzled by (row / 2) mod 8.
+// K half (lane >> 5); ch is the (swizzled) 16-byte chunk index.
 template <int S>
 __device__ __forceinline__ void read_frags(const bf16_t* base, int row0, int ch, bf16x8 (&f)[S]) {
 #pragma unroll
@@ -90,14 +103,121 @@ __device__ __forceinline__ void mma(f32x16 (&acc)[SM][SN], const bf16x8 (&fa)[SM
     for (int j = 0; j < SN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
 }
 
+// Tile (tm, tn) of workgroup blockIdx.x: XCD-contiguous ranges, then
+// GROUP_M-tall groups walked column by column. False for padding workgroups.
+__device__ __forceinline__ bool tile_of_block(const GemmArgs& g, int& tm, int& tn) {
+  const int total = g.tiles_m * g.tiles_n;
+  const int per_xcd = g.grid / N_XCD;
+  const int tile = (blockIdx.x % N_XCD) * per_xcd + blockIdx.x / N_XCD;
+  if (tile >= total) return false;
+  const int group_size = GEMM_GROUP_M * g.tiles_n;
+  const int group = tile / group_size;
+  const int first_m = group * GEMM_GROUP_M;
+  const int gm = min(g.tiles_m - first_m, GEMM_GROUP_M);
+  const int in_group = tile - group * group_size;
+  tm = first_m + in_group % gm;
+  tn = in_group / gm;
+  return true;
+}
+
+// Per-lane byte offsets of the rows this lane copies, one per copy
+// instruction: instruction i of wave w covers rows (w * NI + i) * 8 ..+8;
+// lane l takes row +l/8 and LDS chunk l%8, which holds global chunk
+// (l%8) ^ ((row / 2) mod 8).
+template <int NI>
+struct CopyPlan {
+  uint32_t off[NI];
+};
+
+template <int NI>
+__device__ __forceinline__ CopyPlan<NI> plan_a(const GemmArgs& g, int m0, int M, int wave, int lane) {
+  const int c_row = lane >> 3;
+  CopyPlan<NI> p;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int row0 = (wave * NI + i) * 8;
+    const int ch = (lane & 7) ^ ((c_row >> 1) + ((row0 & 8) ? 4 : 0));
+    p.off[i] = (uint32_t)((g.arow.offset(min(m0 + row0 + c_row, M - 1)) + ch * 8) * 2);
+  }
+  return p;
+}
+
+template <int NI>
+__device__ __forceinline__ CopyPlan<NI> plan_w(const GemmArgs& g, int n0, int wave, int lane) {
+  const int c_row = lane >> 3;
+  CopyPlan<NI> p;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int row0 = (wave * NI + i) * 8;
+    const int ch = (lane & 7) ^ ((c_row >> 1) + ((row0 & 8) ? 4 : 0));
+    p.off[i] = (uint32_t)(((int64_t)min(n0 + row0 + c_row, g.N - 1) * g.ldw + ch * 8) * 2);
+  }
+  return p;
+}
+
+// Epilogue through LDS: a wave stages its fp32 accumulators as 32-row slabs
+// SW columns wide (lane holds column lane&31 and rows 8*(v/4) + 4*(lane>>5) +
+// v%4 of each 32x32 sub-tile), then writes each slab back row-contiguously.
+// Slab rows are padded to SW + 8 floats: lanes 32-63 write 4 rows below lanes
+// 0-31, which then lands on the other half of the 64 banks.
+template <int EPI, int SM, int SN, int SW>
+__device__ __forceinline__ void store_tile(const GemmArgs& g, const f32x16 (&acc)[SM][SN], float* slab, int row0,
+                                           int col0, int lane, int M) {
+  constexpr int LDW = SW + 8, JW = SW / 32;
+  const int fr = lane & 31, fk = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < SM; ++i) {
+#pragma unroll
+    for (int jh = 0; jh < SN / JW; ++jh) {
+#pragma unroll
+      for (int j = 0; j < JW; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          slab[(8 * (v >> 2) + 4 * fk + (v & 3)) * LDW + 32 * j + fr] = acc[i][jh * JW + j][v];
+      wait_lds();   // the slab is written
+      __builtin_amdgcn_wave_barrier();
+      Epilogue<EPI>::template slab32<SW, LDW>(g.epi, slab, row0 + 32 * i, col0 + SW * jh, lane, M, g.N);
+      wait_lds();   // reads done before the next slab overwrites it
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 128x128 tiles, 4 waves (2 x 2), two workgroups per CU.
+// ---------------------------------------------------------------------------
+constexpr int SMALL_THREADS = 256;
+
+// The copies of one slice split in four parts (A rows first, then W rows),
+// spread over the four K steps of the slice being multiplied.
+struct SmallCopy {
+  __amdgpu_buffer_rsrc_t ra, rw;
+  const CopyPlan<4>* pa;
+  const CopyPlan<4>* pw;
+  uint32_t k_bytes;
+  bf16_t* la;
+  bf16_t* lw;
+  int wave;
+  bool live;   // uniform: false when there is no next slice
+  __device__ __forceinline__ void operator()(int q) const {
+    if (!live) return;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int c = q * 2 + j;
+      if (c < 4) copy16(ra, la + (wave * 4 + c) * 8 * GEMM_BK, pa->off[c], k_bytes);
+      else copy16(rw, lw + (wave * 4 + c - 4) * 8 * GEMM_BK, pw->off[c - 4], k_bytes);
+    }
+  }
+};
+
 // One 64-wide K slice from LDS tiles (as, bs). Fragments of step s+1 are read
-// while step s multiplies; the copies of the next slice (if any) are spread
-// over the four steps instead of issued in one burst; the MFMA bursts run at
-// raised wave priority so that, with two workgroups per CU, the SIMD's other
-// wave does its memory work in the gaps. Scheduler barriers pin this order.
-template <int SM, int SN, class Copy>
-__device__ __forceinline__ void slice(f32x16 (&acc)[SM][SN], const bf16_t* as, const bf16_t* bs, int a_row0,
-                                      int b_row0, int fr, int fk, Copy&& copy_part) {
+// while step s multiplies; the copies of the next slice are spread over the
+// four steps; the MFMA bursts run at raised wave priority so that the other
+// workgroup's wave on the SIMD does its memory work in the gaps. Scheduler
+// barriers pin this order.
+template <int SM, int SN>
+__device__ __forceinline__ void small_slice(f32x16 (&acc)[SM][SN], const bf16_t* as, const bf16_t* bs, int a_row0,
+                                            int b_row0, int fr, int fk, const SmallCopy& copy_part) {
   bf16x8 fa0[SM], fb0[SN], fa1[SM], fb1[SN];
   const int sw = (fr >> 1) & 7;   // sub-tile rows start on multiples of 16
   read_frags<SM>(as, a_row0, (0 + fk) ^ sw, fa0);
@@ -132,89 +252,24 @@ __device__ __forceinline__ void slice(f32x16 (&acc)[SM][SN], const bf16_t* as, c
   __builtin_amdgcn_s_setprio(0);
 }
 
-// Part q (0..3) of the copy of one K slice: a quarter of this wave's copy
-// instructions (A rows first, then W rows).
-template <int BM, int BN>
-struct SliceCopy {
-  const bf16_t* A;
-  const bf16_t* W;
-  const CopyPlan<BM>* pa;
-  const CopyPlan<BN>* pb;
-  int k0;
-  bf16_t* la;
-  bf16_t* lb;
-  int wave;
-  bool live;   // uniform: false when there is no next slice
-  __device__ __forceinline__ void operator()(int q) const {
-    constexpr int NA = BM / 32, NB = BN / 32, N = NA + NB, PER = N / 4;
-    static_assert(N % 4 == 0, "copy instructions split into four parts");
-    if (!live) return;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int c = q * PER + j;
-      if (c < NA) {
-        const int row0 = (wave * NA + c) * 8;
-        __builtin_amdgcn_global_load_lds((gbl_void*)(A + pa->off[c] + k0), (lds_void*)(la + row0 * GEMM_BK), 16,
-                                         0, 0);
-      } else {
-        const int cb = c - NA;
-        const int row0 = (wave * NB + cb) * 8;
-        __builtin_amdgcn_global_load_lds((gbl_void*)(W + pb->off[cb] + k0), (lds_void*)(lb + row0 * GEMM_BK), 16,
-                                         0, 0);
-      }
-    }
-  }
-};
-
-template <int BM, int BN, int EPI>
-__global__ __launch_bounds__(GEMM_THREADS) void gemm_bf16_kernel(GemmArgs g) {
-  constexpr int WM = BM / 2, WN = BN / 2;
-  constexpr int SM = WM / 32, SN = WN / 32;   // 32x32 sub-tiles per wave
-  // Two slice buffers, A rows then W rows, as distinct LDS objects.
+template <int EPI>
+__global__ __launch_bounds__(SMALL_THREADS) void gemm_bf16_128_kernel(GemmArgs g) {
+  constexpr int BM = 128, BN = 128, WM = 64, WN = 64;
+  constexpr int SM = WM / 32, SN = WN / 32;
   __shared__ __attribute__((aligned(16))) bf16_t buf0[(BM + BN) * GEMM_BK];
   __shared__ __attribute__((aligned(16))) bf16_t buf1[(BM + BN) * GEMM_BK];
 
-  // ---- tile selection: XCD-contiguous ranges, then GROUP_M-tall groups ----
-  const int total = g.tiles_m * g.tiles_n;
-  const int per_xcd = g.grid / N_XCD;
-  const int tile = (blockIdx.x % N_XCD) * per_xcd + blockIdx.x / N_XCD;
-  if (tile >= total) return;
-  const int group_size = GEMM_GROUP_M * g.tiles_n;
-  const int group = tile / group_size;
-  const int first_m = group * GEMM_GROUP_M;
-  const int gm = min(g.tiles_m - first_m, GEMM_GROUP_M);
-  const int in_group = tile - group * group_size;
-  const int tm = first_m + in_group % gm;
-  const int tn = in_group / gm;
-
+  int tm, tn;
+  if (!tile_of_block(g, tm, tn)) return;
   const int M = g.m_dev ? *g.m_dev : g.M;
   const int m0 = tm * BM, n0 = tn * BN;
   if (m0 >= M) return;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-
-  // ---- copy plans: lane l of an instruction covers row row0 + l/8 (row0 a
-  //      multiple of 8) and LDS chunk l%8, which holds the global chunk
-  //      (l%8) ^ ((row / 2) mod 8) ----
-  const int c_row = lane >> 3;
-  const int c_chunk_lo = (lane & 7) ^ (c_row >> 1);        // rows with (row0/2) % 8 == 0
-  const int c_chunk_hi = (lane & 7) ^ ((c_row >> 1) + 4);  // rows with (row0/2) % 8 == 4
-  CopyPlan<BM> pa;
-  CopyPlan<BN> pb;
-#pragma unroll
-  for (int i = 0; i < BM / 32; ++i) {
-    const int row0 = (wave * (BM / 32) + i) * 8;
-    const int r = row0 + c_row;
-    pa.off[i] = (int32_t)g.arow.offset(min(m0 + r, M - 1)) + ((row0 & 8) ? c_chunk_hi : c_chunk_lo) * 8;
-  }
-#pragma unroll
-  for (int i = 0; i < BN / 32; ++i) {
-    const int row0 = (wave * (BN / 32) + i) * 8;
-    const int r = row0 + c_row;
-    pb.off[i] = (int32_t)((int64_t)min(n0 + r, g.N - 1) * g.ldw) + ((row0 & 8) ? c_chunk_hi : c_chunk_lo) * 8;
-  }
+  const CopyPlan<4> pa = plan_a<4>(g, m0, M, wave, lane);
+  const CopyPlan<4> pw = plan_w<4>(g, n0, wave, lane);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.A, g.a_bytes), rw = make_rsrc(g.W, g.w_bytes);
 
   f32x16 acc[SM][SN];
 #pragma unroll
@@ -233,83 +288,241 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_bf16_kernel(GemmArgs g) {
   bf16_t* const b1 = buf1 + BM * GEMM_BK;
 
   const int nk = g.K / GEMM_BK;
-  copy_slice<BM>(g.A, pa, 0, a0, wave);
-  copy_slice<BN>(g.W, pb, 0, b0, wave);
+  {
+    const SmallCopy first{ra, rw, &pa, &pw, 0, a0, b0, wave, true};
+    first(0);
+    first(1);
+    first(2);
+    first(3);
+  }
   wait_copies();
   __syncthreads();
 
   int kt = 0;
   for (; kt + 1 < nk; kt += 2) {
     // slice kt from buffer 0 while slice kt+1 lands in buffer 1
-    slice<SM, SN>(acc, a0, b0, a_row0, b_row0, fr, fk,
-                  SliceCopy<BM, BN>{g.A, g.W, &pa, &pb, (kt + 1) * GEMM_BK, a1, b1, wave, true});
+    small_slice<SM, SN>(acc, a0, b0, a_row0, b_row0, fr, fk,
+                        SmallCopy{ra, rw, &pa, &pw, (uint32_t)(kt + 1) * GEMM_BK * 2, a1, b1, wave, true});
     wait_copies();
     __syncthreads();
     // slice kt+1 from buffer 1 while slice kt+2 (if any) lands in buffer 0
-    slice<SM, SN>(acc, a1, b1, a_row0, b_row0, fr, fk,
-                  SliceCopy<BM, BN>{g.A, g.W, &pa, &pb, (kt + 2) * GEMM_BK, a0, b0, wave, kt + 2 < nk});
+    small_slice<SM, SN>(acc, a1, b1, a_row0, b_row0, fr, fk,
+                        SmallCopy{ra, rw, &pa, &pw, (uint32_t)(kt + 2) * GEMM_BK * 2, a0, b0, wave, kt + 2 < nk});
     wait_copies();
     __syncthreads();
   }
   if (kt < nk) {   // odd slice count: the last slice sits in buffer 0
-    slice<SM, SN>(acc, a0, b0, a_row0, b_row0, fr, fk,
-                  SliceCopy<BM, BN>{g.A, g.W, &pa, &pb, 0, a1, b1, wave, false});
+    small_slice<SM, SN>(acc, a0, b0, a_row0, b_row0, fr, fk, SmallCopy{ra, rw, &pa, &pw, 0, a1, b1, wave, false});
     __syncthreads();
   }
 
-  // ---- epilogue through LDS: each wave stages 32-row slabs of its fp32 tile
-  //      (lane holds column lane&31 and rows 8*(v/4) + 4*(lane>>5) + v%4 of each
-  //      32x32 sub-tile), then writes them back row-contiguously ----
-  // Slab rows padded to WN + 8 floats: lanes 32-63 write 4 rows below lanes
-  // 0-31, which then lands on the other half of the 64 banks.
-  constexpr int LDW = WN + 8;
-  float* slab = (float*)(wave < 2 ? buf0 : buf1) + (wave & 1) * (32 * LDW);
-  const int col0 = n0 + wn * WN;
-#pragma unroll
-  for (int i = 0; i < SM; ++i) {
-#pragma unroll
-    for (int j = 0; j < SN; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) slab[(8 * (v >> 2) + 4 * fk + (v & 3)) * LDW + 32 * j + fr] = acc[i][j][v];
-    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the slab is written
-    __builtin_amdgcn_wave_barrier();
-    Epilogue<EPI>::template slab32<WN, LDW>(g.epi, slab, m0 + wm * WM + 32 * i, col0, lane, M, g.N);
-    __builtin_amdgcn_s_waitcnt(0xc07f);   // reads done before the next slab overwrites it
-    __builtin_amdgcn_wave_barrier();
-  }
+  constexpr int SW = WN;
+  float* slab = (float*)(wave < 2 ? buf0 : buf1) + (wave & 1) * (32 * (SW + 8));
+  store_tile<EPI, SM, SN, SW>(g, acc, slab, m0 + wm * WM, n0 + wn * WN, lane, M);
 }
 
-template <int BM, int BN, int EPI>
-static hipError_t launch_cfg(const GemmArgs& in, hipStream_t stream) {
-  GemmArgs g = in;
-  g.tiles_m = (g.M + BM - 1) / BM;
-  g.tiles_n = (g.N + BN - 1) / BN;
-  const int total = g.tiles_m * g.tiles_n;
-  g.grid = (total + N_XCD - 1) / N_XCD * N_XCD;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, EPI>), dim3(g.grid), dim3(GEMM_THREADS), 0, stream, g);
-  return hipGetLastError();
+// ---------------------------------------------------------------------------
+// 256x256 tiles, 8 waves (4 x 2) in two ping-pong groups, one workgroup per CU.
+// ---------------------------------------------------------------------------
+constexpr int BIG_THREADS = 512;
+
+// Fragments of half a slice (two K steps).
+template <int SM, int SN>
+__device__ __forceinline__ void read_half(const bf16_t* as, const bf16_t* bs, int a_row0, int b_row0, int sw,
+                                          int fk, int h, bf16x8 (&fa)[2][SM], bf16x8 (&fb)[2][SN]) {
+  read_frags<SM>(as, a_row0, (4 * h + 0 + fk) ^ sw, fa[0]);
+  read_frags<SN>(bs, b_row0, (4 * h + 0 + fk) ^ sw, fb[0]);
+  read_frags<SM>(as, a_row0, (4 * h + 2 + fk) ^ sw, fa[1]);
+  read_frags<SN>(bs, b_row0, (4 * h + 2 + fk) ^ sw, fb[1]);
+}
+
+template <int SM, int SN>
+__device__ __forceinline__ void compute_half(f32x16 (&acc)[SM][SN], const bf16x8 (&fa)[2][SM],
+                                             const bf16x8 (&fb)[2][SN]) {
+  __builtin_amdgcn_s_setprio(1);
+  mma<SM, SN>(acc, fa[0], fb[0]);
+  mma<SM, SN>(acc, fa[1], fb[1]);
+  __builtin_amdgcn_s_setprio(0);
+}
+
+struct BigCopy {
+  __amdgpu_buffer_rsrc_t ra, rw;
+  CopyPlan<4> pa, pw;
+  int wave;
+  // this wave's 8 copy instructions of the slice at K byte offset k_bytes
+  __device__ __forceinline__ void slice(uint32_t k_bytes, bf16_t* la, bf16_t* lw) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) copy16(ra, la + (wave * 4 + i) * 8 * GEMM_BK, pa.off[i], k_bytes);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) copy16(rw, lw + (wave * 4 + i) * 8 * GEMM_BK, pw.off[i], k_bytes);
+  }
+};
+
+// One K slice in four phases, each closed by a workgroup barrier. Group 0
+// reads fragments (half 0, then half 1) in phases 0 and 2 and multiplies in
+// 1 and 3; group 1 runs one phase later (its phase-0 work is the second half
+// of the previous slice). Both groups copy the next slice into the other
+// buffer as they start reading this one (its last readers finished in the
+// previous slice's phase 3) and wait for their copies at the end of phase 3.
+template <int G, int SM, int SN>
+__device__ __forceinline__ void big_slice(f32x16 (&acc)[SM][SN], bf16x8 (&fa)[2][SM], bf16x8 (&fb)[2][SN],
+                                          const bf16_t* ca, const bf16_t* cb, bf16_t* na, bf16_t* nb, int a_row0,
+                                          int b_row0, int sw, int fk, const BigCopy& cp, uint32_t k_next,
+                                          bool live, bool first) {
+  // phase 0
+  if (G == 0) {
+    if (live) cp.slice(k_next, na, nb);
+    read_half<SM, SN>(ca, cb, a_row0, b_row0, sw, fk, 0, fa, fb);
+    wait_lds();
+  } else if (!first) {
+    compute_half<SM, SN>(acc, fa, fb);
+  }
+  AENC_BARRIER();
+  // phase 1
+  if (G == 0) {
+    compute_half<SM, SN>(acc, fa, fb);
+  } else {
+    if (live) cp.slice(k_next, na, nb);
+    read_half<SM, SN>(ca, cb, a_row0, b_row0, sw, fk, 0, fa, fb);
+    wait_lds();
+  }
+  AENC_BARRIER();
+  // phase 2
+  if (G == 0) {
+    read_half<SM, SN>(ca, cb, a_row0, b_row0, sw, fk, 1, fa, fb);
+    wait_lds();
+  } else {
+    compute_half<SM, SN>(acc, fa, fb);
+  }
+  AENC_BARRIER();
+  // phase 3
+  if (G == 0) {
+    compute_half<SM, SN>(acc, fa, fb);
+  } else {
+    read_half<SM, SN>(ca, cb, a_row0, b_row0, sw, fk, 1, fa, fb);
+    wait_lds();
+  }
+  wait_copies();
+  AENC_BARRIER();
+}
+
+template <int G, int SM, int SN>
+__device__ __forceinline__ void big_loop(f32x16 (&acc)[SM][SN], bf16_t* a0, bf16_t* b0, bf16_t* a1, bf16_t* b1,
+                                         int a_row0, int b_row0, int sw, int fk, const BigCopy& cp, int nk) {
+  bf16x8 fa[2][SM], fb[2][SN];
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    big_slice<G, SM, SN>(acc, fa, fb, a0, b0, a1, b1, a_row0, b_row0, sw, fk, cp, (uint32_t)(kt + 1) * GEMM_BK * 2,
+                         true, kt == 0);
+    big_slice<G, SM, SN>(acc, fa, fb, a1, b1, a0, b0, a_row0, b_row0, sw, fk, cp, (uint32_t)(kt + 2) * GEMM_BK * 2,
+                         kt + 2 < nk, false);
+  }
+  if (kt < nk)   // odd slice count: the last slice sits in buffer 0
+    big_slice<G, SM, SN>(acc, fa, fb, a0, b0, a1, b1, a_row0, b_row0, sw, fk, cp, 0, false, kt == 0);
+  if (G == 1) compute_half<SM, SN>(acc, fa, fb);   // group 1's last half slice
+  AENC_BARRIER();
 }
 
 template <int EPI>
-static hipError_t launch_epi(const GemmArgs& g, int tile_cfg, hipStream_t stream) {
-  switch (tile_cfg) {
-    case GEMM_TILE_256x256: return launch_cfg<256, 256, EPI>(g, stream);
-    case GEMM_TILE_256x128: return launch_cfg<256, 128, EPI>(g, stream);
-    case GEMM_TILE_128x128: return launch_cfg<128, 128, EPI>(g, stream);
-    default: return hipErrorInvalidValue;
-  }
+__global__ __launch_bounds__(BIG_THREADS) void gemm_bf16_256_kernel(GemmArgs g) {
+  constexpr int BM = 256, BN = 256, WM = 64, WN = 128;
+  constexpr int SM = WM / 32, SN = WN / 32;
+  __shared__ __attribute__((aligned(16))) bf16_t buf0[(BM + BN) * GEMM_BK];
+  __shared__ __attribute__((aligned(16))) bf16_t buf1[(BM + BN) * GEMM_BK];
+
+  int tm, tn;
+  if (!tile_of_block(g, tm, tn)) return;
+  const int M = g.m_dev ? *g.m_dev : g.M;
+  const int m0 = tm * BM, n0 = tn * BN;
+  if (m0 >= M) return;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  BigCopy cp;
+  cp.ra = make_rsrc(g.A, g.a_bytes);
+  cp.rw = make_rsrc(g.W, g.w_bytes);
+  cp.pa = plan_a<4>(g, m0, M, wave, lane);
+  cp.pw = plan_w<4>(g, n0, wave, lane);
+  cp.wave = wave;
+
+  f32x16 acc[SM][SN];
+#pragma unroll
+  for (int i = 0; i < SM; ++i)
+#pragma unroll
+    for (int j = 0; j < SN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  const int fr = lane & 31, fk = lane >> 5;
+  const int a_row0 = wm * WM + fr;
+  const int b_row0 = wn * WN + fr;
+  const int sw = (fr >> 1) & 7;
+  bf16_t* const a0 = buf0;
+  bf16_t* const b0 = buf0 + BM * GEMM_BK;
+  bf16_t* const a1 = buf1;
+  bf16_t* const b1 = buf1 + BM * GEMM_BK;
+  const int nk = g.K / GEMM_BK;
+
+  cp.slice(0, a0, b0);
+  wait_copies();
+  AENC_BARRIER();
+  if (wave < 4)
+    big_loop<0, SM, SN>(acc, a0, b0, a1, b1, a_row0, b_row0, sw, fk, cp, nk);
+  else
+    big_loop<1, SM, SN>(acc, a0, b0, a1, b1, a_row0, b_row0, sw, fk, cp, nk);
+
+  constexpr int SW = 64;
+  float* slab = (float*)(wave < 4 ? buf0 : buf1) + (wave & 3) * (32 * (SW + 8));
+  store_tile<EPI, SM, SN, SW>(g, acc, slab, m0 + wm * WM, n0 + wn * WN, lane, M);
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+template <int EPI>
+static hipError_t launch_epi(GemmArgs g, int tile_cfg, hipStream_t stream) {
+  const int bt = tile_cfg == GEMM_TILE_256x256 ? 256 : 128;
+  g.tiles_m = (g.M + bt - 1) / bt;
+  g.tiles_n = (g.N + bt - 1) / bt;
+  const int total = g.tiles_m * g.tiles_n;
+  g.grid = (total + N_XCD - 1) / N_XCD * N_XCD;
+  if (tile_cfg == GEMM_TILE_256x256)
+    hipLaunchKernelGGL((gemm_bf16_256_kernel<EPI>), dim3(g.grid), dim3(BIG_THREADS), 0, stream, g);
+  else
+    hipLaunchKernelGGL((gemm_bf16_128_kernel<EPI>), dim3(g.grid), dim3(SMALL_THREADS), 0, stream, g);
+  return hipGetLastError();
+}
+
+int gemm_pick_tile(int M, int N) {
+  // The 256x256 kernel is faster per tile but runs one workgroup per CU: use
+  // it when its tiles fill the 256 CUs at least once.
+  const int64_t big_tiles = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
+  return big_tiles >= 256 ? GEMM_TILE_256x256 : GEMM_TILE_128x128;
+}
+
+// Largest element offset (+1) reachable through a row map over rows [0, M).
+static int64_t row_extent(const RowMap& r, int M, int K) {
+  if (r.rpg == INT32_MAX) return (int64_t)(M - 1) * r.rstride + r.off + K;
+  const int64_t groups = (M - 1) / r.rpg;
+  return groups * r.gstride + (int64_t)(r.rpg - 1) * r.rstride + r.off + K;
 }
 
 hipError_t gemm_bf16(int epi, const bf16_t* A, RowMap arow, const bf16_t* W, int64_t ldw, int M, int N, int K,
                      const int32_t* m_dev, const EpiParams& ep, int tile_cfg, hipStream_t stream) {
   // K in whole slices; N in groups of 4 (the epilogue writes 4 columns per lane).
   if (K % GEMM_BK != 0 || M <= 0 || N <= 0 || N % 4 != 0) return hipErrorInvalidValue;
-  // V columns of the QKV epilogue start on a wave boundary.
+  if (tile_cfg != GEMM_TILE_256x256 && tile_cfg != GEMM_TILE_128x128) return hipErrorInvalidValue;
+  // V columns of the QKV epilogue start on a slab boundary.
   if (epi == EPI_QKV_BF16 && ep.n_split % 128 != 0) return hipErrorInvalidValue;
-  // The copy plans hold 32-bit element offsets.
-  if ((int64_t)N * ldw >= INT32_MAX) return hipErrorInvalidValue;
+  // A is addressed through a closed-form row map (no per-row table), and the
+  // copies use 32-bit byte offsets.
+  if (arow.map) return hipErrorInvalidValue;
+  const int64_t a_elems = row_extent(arow, M, K), w_elems = (int64_t)(N - 1) * ldw + K;
+  if (a_elems * 2 >= (int64_t)UINT32_MAX || w_elems * 2 >= (int64_t)UINT32_MAX) return hipErrorInvalidValue;
   GemmArgs g{};
   g.A = A; g.arow = arow; g.W = W; g.ldw = ldw; g.M = M; g.N = N; g.K = K; g.m_dev = m_dev; g.epi = ep;
+  g.a_bytes = (uint32_t)(a_elems * 2);
+  g.w_bytes = (uint32_t)(w_elems * 2);
   switch (epi) {
     case EPI_STORE_BF16: return launch_epi<EPI_STORE_BF16>(g, tile_cfg, stream);
     case EPI_GELU_BF16: return launch_epi<EPI_GELU_BF16>(g, tile_cfg, stream);

@@ -40,8 +40,8 @@ extern "C" int aenc_k_gemm_bf16(int epi, const void* A, int64_t lda, const void*
     case AENC_EPI_F32: kind = EPI_STORE_F32; break;
     default: return fail("unknown epilogue");
   }
-  if (tile < 0) tile = GEMM_TILE_256x128;
-  if (tile > GEMM_TILE_128x128) return fail("unknown tile");
+  if (tile < 0) tile = gemm_pick_tile(M, N);
+  if (tile != GEMM_TILE_256x256 && tile != GEMM_TILE_128x128) return fail("unknown tile");
   EpiParams ep{};
   ep.bias = bias;
   ep.c = C;
@@ -62,7 +62,7 @@ extern "C" int aenc_k_qkv_bf16(const void* A, const void* Wqkv, const float* bia
   ep.vt = (bf16_t*)vt;
   ep.ld_vt = ld_vt;
   return hip_status(gemm_bf16(EPI_QKV_BF16, (const bf16_t*)A, dense_rows(d), (const bf16_t*)Wqkv, d, M, 3 * d, d,
-                              nullptr, ep, GEMM_TILE_256x128, (hipStream_t)stream), "qkv");
+                              nullptr, ep, gemm_pick_tile(M, 3 * d), (hipStream_t)stream), "qkv");
 }
 
 extern "C" int aenc_k_attention_bf16(const void* qk, const void* vt, int64_t ld_vt, const int32_t* start,

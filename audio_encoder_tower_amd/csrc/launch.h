@@ -6,11 +6,14 @@
 
 namespace aenc {
 
-enum GemmTile { GEMM_TILE_256x256 = 0, GEMM_TILE_256x128 = 1, GEMM_TILE_128x128 = 2 };
+enum GemmTile { GEMM_TILE_256x256 = 0, GEMM_TILE_128x128 = 1 };
 
 // bf16 MFMA GEMM, C = epi(A W^T + b); K % 64 == 0.
 hipError_t gemm_bf16(int epi, const bf16_t* A, RowMap arow, const bf16_t* W, int64_t ldw, int M, int N, int K,
                      const int32_t* m_dev, const EpiParams& ep, int tile_cfg, hipStream_t stream);
+
+// The tile shape gemm_bf16 runs fastest with for an M x N output.
+int gemm_pick_tile(int M, int N);
 
 // fp32 GEMM on the vector ALUs (the fp32 path), same epilogues; K % 16 == 0.
 hipError_t gemm_f32(int epi, const float* A, RowMap arow, const float* W, int64_t ldw, int M, int N, int K,

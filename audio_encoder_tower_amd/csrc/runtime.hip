@@ -518,14 +518,7 @@ struct Enq {
   }
 };
 
-int pick_tile(int M, int N) {
-  // 128x128 tiles run two workgroups per CU (their LDS and registers fit
-  // twice), which hides the slice copies behind the other workgroup's MFMAs;
-  // on the encoder's shapes they beat the larger tiles (measured on MI355X).
-  (void)M;
-  (void)N;
-  return GEMM_TILE_128x128;
-}
+int pick_tile(int M, int N) { return gemm_pick_tile(M, N); }
 
 }  // namespace
 

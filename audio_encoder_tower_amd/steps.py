@@ -13,7 +13,7 @@ import torch
 from ._lib import check, lib
 
 EPI = {"bf16": 0, "gelu_bf16": 1, "resid_f32": 2, "f32": 3}
-TILE = {"auto": -1, "256x256": 0, "256x128": 1, "128x128": 2}
+TILE = {"auto": -1, "256x256": 0, "128x128": 1}
 
 
 def _p(t: Optional[torch.Tensor]):

@@ -30,8 +30,9 @@ enum {
   AENC_EPI_F32 = 3        /* C (fp32) = A W^T + b                     */
 };
 
-/* Tile shapes of aenc_k_gemm_bf16 (-1 = the library's choice). */
-enum { AENC_TILE_256x256 = 0, AENC_TILE_256x128 = 1, AENC_TILE_128x128 = 2 };
+/* Tile shapes of aenc_k_gemm_bf16 (-1 = the library's choice): 256x256 output
+ * tiles on 8 waves (one workgroup per CU) or 128x128 tiles on 4 waves. */
+enum { AENC_TILE_256x256 = 0, AENC_TILE_128x128 = 1 };
 
 /* C[M, N] = epi(A[M, K] W[N, K]^T + bias[N]) with bf16 A and W (row-major,
  * leading dimensions lda, K and ldc in elements), fp32 accumulate.

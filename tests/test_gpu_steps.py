@@ -45,13 +45,11 @@ GEMM_SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("tile", ["256x256", "256x128", "128x128"])
+@pytest.mark.parametrize("tile", ["256x256", "128x128"])
 @pytest.mark.parametrize("epi", ["bf16", "gelu_bf16", "resid_f32", "f32"])
 @pytest.mark.parametrize("shape", GEMM_SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_gemm_bf16(_lib, shape, epi, tile):
     M, N, K = shape
-    if M * N * K > 2e9 and tile != "256x128":
-        pytest.skip("large shapes checked with one tile shape")
     print(f"gemm {shape} {epi} {tile}", flush=True)
     rng = np.random.default_rng(hash((M, N, K)) % 2**32)
     a, w = bf16(rng, M, K), bf16(rng, N, K, scale=0.05)
