@@ -184,13 +184,33 @@ def stem(mel: np.ndarray, W: Dict[str, np.ndarray], dtype=np.float64) -> np.ndar
     return xt + sinusoids(xt.shape[0], xt.shape[1], dtype)
 
 
+def stack_rows(y: np.ndarray, k: int) -> np.ndarray:
+    """Concatenate each run of k consecutive positions into one row:
+    row j = [y[k j], y[k j + 1], ..., y[k j + k - 1]]; a trailing partial run
+    is dropped.
+
+    Whisper features downsampled from 50 to 12.5 positions per second
+    ("[WIP][TSS][Model] Kimi-Audio-7B", Purpose, Audio Tokenizer) into an
+    adaptor input of 5120 = 4 x 1280 ("Kimi-Audio-7B-Instruct", (1) AUDIO,
+    kimia_adaptor_input_dim).
+    """
+    n, d = y.shape[0] // k, y.shape[1]
+    out = np.empty((n, k * d), dtype=y.dtype)
+    for j in range(n):
+        for i in range(k):
+            out[j, i * d:(i + 1) * d] = y[k * j + i]
+    return out
+
+
 def final(x: np.ndarray, W: Dict[str, np.ndarray], pool_step: int = 1, eps: float = LN_EPS,
-          dtype=np.float64) -> np.ndarray:
+          dtype=np.float64, stack: int = 1) -> np.ndarray:
     """Final LayerNorm, then the optional pool or projector.
 
     pool_step 2 averages positions (2j, 2j+1), j < floor(T/2) ("MiniCPM-o-2_6",
     "(2) AUDIO": audio_pool_step 2, 1500 -> ~750). The projector is
-    GELU(Y Wp1^T + bp1) Wp2^T + bp2 ("Voxtral-Mini-3B-2507", "PROJECTOR").
+    GELU(Y Wp1^T + bp1) Wp2^T + bp2 ("Voxtral-Mini-3B-2507", "PROJECTOR");
+    with stack > 1 its input rows are runs of `stack` consecutive positions
+    (stack_rows).
     """
     y = layer_norm(x, _f(W["lnf_g"], dtype), _f(W["lnf_b"], dtype), eps)
     if pool_step == 2:
@@ -198,6 +218,10 @@ def final(x: np.ndarray, W: Dict[str, np.ndarray], pool_step: int = 1, eps: floa
         y = (y[0:2 * n:2] + y[1:2 * n:2]) / 2.0
     elif pool_step != 1:
         raise ValueError("pool_step must be 1 or 2")
+    if stack != 1:
+        if pool_step != 1 or "proj1_w" not in W:
+            raise ValueError("stacking feeds the projector and is not combined with the pool")
+        y = stack_rows(y, stack)
     if "proj1_w" in W:
         if pool_step != 1:
             raise ValueError("pool and projector together are not defined")
@@ -214,7 +238,7 @@ def encode_clip(geom, W: Dict[str, np.ndarray], mel: np.ndarray,
     depth = geom.n_layers if n_layers is None else n_layers
     x = stem(mel, W, dtype)
     x = blocks(x, W, depth, geom.n_heads, key_mask, geom.ln_eps, dtype)
-    return final(x, W, geom.pool_step, geom.ln_eps, dtype)
+    return final(x, W, geom.pool_step, geom.ln_eps, dtype, getattr(geom, "stack", 1))
 
 
 def encode(geom, W: Dict[str, np.ndarray], mel: np.ndarray, mask: Optional[np.ndarray] = None,
@@ -247,7 +271,7 @@ def param_shapes(geom) -> List[Tuple[str, Tuple[int, ...]]]:
                    (p + "fc1_w", (f, d)), (p + "fc1_b", (f,)), (p + "fc2_w", (d, f)), (p + "fc2_b", (d,))]
     shapes += [("lnf_g", (d,)), ("lnf_b", (d,))]
     if geom.proj_hidden:
-        shapes += [("proj1_w", (geom.proj_hidden, d)), ("proj1_b", (geom.proj_hidden,)),
+        shapes += [("proj1_w", (geom.proj_hidden, getattr(geom, "stack", 1) * d)), ("proj1_b", (geom.proj_hidden,)),
                    ("proj2_w", (geom.proj_out, geom.proj_hidden)), ("proj2_b", (geom.proj_out,))]
     return shapes
 
@@ -274,5 +298,6 @@ def flops(geom, frames: Optional[Sequence[int]] = None) -> float:
         per_layer = 2.0 * tb * (3 * d * d + d * d + 2 * d * f) + 4.0 * tb * tb * d
         total += geom.n_layers * per_layer
         if geom.proj_hidden:
-            total += 2.0 * tb * (d * geom.proj_hidden + geom.proj_hidden * geom.proj_out)
+            k = getattr(geom, "stack", 1)
+            total += 2.0 * (tb // k) * (k * d * geom.proj_hidden + geom.proj_hidden * geom.proj_out)
     return total

@@ -56,7 +56,7 @@ def weight_shapes(g: Geometry) -> List[Tuple[str, Tuple[int, ...]]]:
 def proj_shapes(g: Geometry) -> List[Tuple[str, Tuple[int, ...]]]:
     if not g.has_projector:
         return []
-    return [("proj1_w", (g.proj_hidden, g.d_model)), ("proj1_b", (g.proj_hidden,)),
+    return [("proj1_w", (g.proj_hidden, g.proj_in)), ("proj1_b", (g.proj_hidden,)),
             ("proj2_w", (g.proj_out, g.proj_hidden)), ("proj2_b", (g.proj_out,))]
 
 

@@ -11,6 +11,10 @@ Geometry facts come from the model records on the pages:
     audio_pool_step 2: "MiniCPM-o-2_6", section "(2) AUDIO".
   * 2-layer GELU projector into the 3072-wide LLM: "Voxtral-Mini-3B-2507",
     section "PROJECTOR".
+  * Stacking 4 consecutive encoder positions into one 5120-wide projector
+    input (50 -> 12.5 positions per second): Whisper features downsampled to
+    12.5 Hz ("[WIP][TSS][Model] Kimi-Audio-7B", Purpose, Audio Tokenizer),
+    kimia_adaptor_input_dim 5120 ("Kimi-Audio-7B-Instruct", (1) AUDIO).
 
 A workload is named for what it is and fixes the seeds of every tensor.
 """
@@ -38,6 +42,7 @@ class Geometry:
     dtype: str = BF16      # weights, mel and activations
     out_dtype: str = F32
     ln_eps: float = 1e-5
+    stack: int = 1         # positions concatenated into one projector input row (1 or 4)
 
     @property
     def n_pos(self) -> int:
@@ -54,7 +59,12 @@ class Geometry:
 
     @property
     def t_out(self) -> int:
-        return self.n_pos // self.pool_step
+        return self.n_pos // self.pool_step // self.stack
+
+    @property
+    def proj_in(self) -> int:
+        """Width of a projector input row: stack consecutive positions."""
+        return self.stack * self.d_model
 
     @property
     def d_out(self) -> int:
@@ -110,6 +120,12 @@ WORKLOADS: Dict[str, Workload] = {
             "whisper_large_proj_b16",
             Geometry(batch=16, proj_hidden=3072, proj_out=3072, **WHISPER_LARGE),
             description="Whisper-large encoder, bf16, batch 16, GELU projector 1280->3072->3072",
+        ),
+        Workload(
+            "whisper_large_stack4_proj_b16",
+            Geometry(batch=16, proj_hidden=3072, proj_out=3072, stack=4, **WHISPER_LARGE),
+            description="Whisper-large encoder, bf16, batch 16, 4 positions stacked (12.5 Hz) into a "
+                        "GELU projector 5120->3072->3072",
         ),
         Workload(
             "whisper_large_varlen_b32",

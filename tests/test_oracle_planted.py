@@ -12,7 +12,8 @@ import pytest
 import oracle
 import synth
 from oracle import encoder as E
-from tests.test_oracle_pins import TOWER_CASES, _float64_modules, tiny_workload, torch_encoder  # noqa: F401
+from tests.test_oracle_pins import (TOWER_CASES, _float64_modules, tiny_workload, torch_encoder,  # noqa: F401
+                                    valid_out_rows)
 
 
 def _tower_pins_pass() -> bool:
@@ -34,14 +35,16 @@ def _tower_pins_pass() -> bool:
         ref = torch_encoder(g, W, mel, mask)
         if got.shape != ref.shape:
             return False
-        rows = np.ones(got.shape[:2], bool) if mask is None else mask.astype(bool)
-        if not np.allclose(got[rows], ref[rows], rtol=1e-10, atol=1e-11):
-            return False
+        for b in range(g.batch):
+            v = valid_out_rows(g, mask, b)
+            if not np.allclose(got[b][v], ref[b][v], rtol=1e-10, atol=1e-11):
+                return False
     return True
 
 
 real = {name: getattr(E, name) for name in
-        ("gelu", "layer_norm", "linear", "conv1d_k3", "sinusoids", "attention", "block", "final", "stem")}
+        ("gelu", "layer_norm", "linear", "conv1d_k3", "sinusoids", "attention", "block", "final", "stem",
+         "stack_rows")}
 
 
 def m_unbiased_var(x, g, b, eps=E.LN_EPS):
@@ -113,6 +116,18 @@ def m_no_pe(mel, W, dtype=np.float64):
     return x - real["sinusoids"](x.shape[0], x.shape[1], dtype)
 
 
+def m_stack_feature_major(y, k):
+    # interleaves the k positions feature by feature instead of concatenating them
+    n, d = y.shape[0] // k, y.shape[1]
+    return y[:n * k].reshape(n, k, d).transpose(0, 2, 1).reshape(n, k * d)
+
+
+def m_stack_keeps_partial_run(y, k):
+    n, d = -(-y.shape[0] // k), y.shape[1]
+    pad = np.zeros((n * k - y.shape[0], d))
+    return real["stack_rows"](np.concatenate([y, pad]), k)
+
+
 MUTATIONS = {
     "unbiased_variance": ("layer_norm", m_unbiased_var),
     "tanh_gelu": ("gelu", m_tanh_gelu),
@@ -126,6 +141,8 @@ MUTATIONS = {
     "ffn_residual_dropped": ("block", m_no_ffn_residual),
     "pool_before_final_ln": ("final", m_pool_before_ln),
     "positions_not_added": ("stem", m_no_pe),
+    "stack_feature_major": ("stack_rows", m_stack_feature_major),
+    "stack_keeps_partial_run": ("stack_rows", m_stack_keeps_partial_run),
 }
 
 
