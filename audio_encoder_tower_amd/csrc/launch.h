@@ -57,6 +57,15 @@ hipError_t mel_transpose(const void* mel, int in_dtype, void* melT, int B, int C
 hipError_t build_row_maps(const uint8_t* mask, int B, int T, int32_t* row_map, int32_t* inv_map, int32_t* cu,
                           int32_t* lens, int32_t* m_valid, hipStream_t stream);
 
+// Maps of the stacked projector rows from the clip starts and lengths:
+// stacked row r holds packed rows k r .. k r + k - 1. row_map [B * (T / k)]:
+// output row b * (T/k) + j -> stacked row cu[b] / k + j when its k positions
+// are all valid (k j + k <= lens[b]), else -1. inv_map [B * round_up(T, 8) / k]:
+// the inverse, -1 for stacked rows that are no output row. m_valid [1]:
+// stacked rows to compute, ceil(cu[B] / k). k divides 8.
+hipError_t build_stack_maps(const int32_t* cu, const int32_t* lens, int B, int T, int k, int32_t* row_map,
+                            int32_t* inv_map, int32_t* m_valid, hipStream_t stream);
+
 // Repack conv weight [out, in, 3] (dtype) -> [out, 3, in_pad] in the same dtype.
 hipError_t repack_conv(const void* src, int dtype, void* dst, int out, int in, int in_pad, hipStream_t stream);
 

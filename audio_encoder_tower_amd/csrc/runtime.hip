@@ -89,6 +89,9 @@ struct aenc_handle {
   int32_t *row_map = nullptr, *inv_map = nullptr, *cu = nullptr, *lens = nullptr, *m_valid = nullptr;
   int32_t *id_row_map = nullptr, *id_inv_map = nullptr, *id_cu = nullptr, *id_lens = nullptr,
           *id_m_valid = nullptr;
+  // stacked projector rows (stack > 1): output row -> stacked row, stacked row -> output row, row count
+  int32_t *sk_row_map = nullptr, *sk_inv_map = nullptr, *sk_m_valid = nullptr;
+  int32_t *id_sk_row_map = nullptr, *id_sk_inv_map = nullptr, *id_sk_m_valid = nullptr;
 
   // profiling
   bool prof = false;
@@ -143,8 +146,25 @@ extern "C" int aenc_validate(const aenc_geometry* g) {
     set_error("pool_step 2 together with a projector is not defined");
     return AENC_E_UNSUPPORTED;
   }
+  if (g->stack != 0 && g->stack != 1 && g->stack != 4) {
+    set_error("stack %d must be 0, 1 or 4", g->stack);
+    return AENC_E_INVAL;
+  }
+  if (g->stack == 4 && !proj) {
+    set_error("stack 4 feeds the projector: set proj_hidden and proj_out");
+    return AENC_E_UNSUPPORTED;
+  }
+  if (g->stack == 4 && g->n_frames / 2 < 4) {
+    set_error("stack 4 needs at least 4 positions (n_frames >= 8)");
+    return AENC_E_INVAL;
+  }
   return AENC_OK;
 }
+
+namespace {
+// Positions concatenated into one projector input row (0 means 1).
+int stack_of(const aenc_geometry* g) { return g->stack > 1 ? g->stack : 1; }
+}  // namespace
 
 extern "C" int64_t aenc_param_count(const aenc_geometry* g) {
   if (aenc_validate(g) != AENC_OK) return -1;
@@ -152,7 +172,8 @@ extern "C" int64_t aenc_param_count(const aenc_geometry* g) {
   int64_t n = 3 * m * d + d + 3 * d * d + d;                         // conv stem
   n += L * (4 * d * d + 3 * d + 2 * d * f + f + d + 4 * d);          // blocks (no key bias)
   n += 2 * d;                                                        // final LN
-  if (g->proj_hidden) n += d * g->proj_hidden + g->proj_hidden + (int64_t)g->proj_hidden * g->proj_out + g->proj_out;
+  if (g->proj_hidden)
+    n += stack_of(g) * d * g->proj_hidden + g->proj_hidden + (int64_t)g->proj_hidden * g->proj_out + g->proj_out;
   return n;
 }
 
@@ -161,7 +182,7 @@ extern "C" int aenc_output_shape(const aenc_geometry* g, int64_t shape[3]) {
   if (st != AENC_OK) return st;
   if (!shape) { set_error("shape is NULL"); return AENC_E_INVAL; }
   shape[0] = g->batch;
-  shape[1] = (g->n_frames / 2) / g->pool_step;
+  shape[1] = (g->n_frames / 2) / g->pool_step / stack_of(g);
   shape[2] = g->proj_hidden ? g->proj_out : g->d_model;
   return AENC_OK;
 }
@@ -195,9 +216,12 @@ Layout workspace_layout(const aenc_geometry* g) {
   L.off_qk = take(L.M_cap * (g->dtype == AENC_BF16 ? 2 : 3) * d * L.esz);
   L.off_vt = take(g->dtype == AENC_BF16 ? d * L.ld_vt * 2 : 0);
   L.off_hmid = take(L.M_cap * mid * L.esz);
-  // row_map, inv_map, cu, lens, m_valid twice (per-forward and all-valid)
+  // row_map, inv_map, cu, lens, m_valid twice (per-forward and all-valid),
+  // then the stacked-row maps twice when the projector reads stacked rows
+  const int k = stack_of(g);
   const size_t maps = (size_t)(B * L.T + L.M_cap + (B + 1) + B + 1) * 4;
-  L.off_maps = take(2 * maps + 64);
+  const size_t sk_maps = k > 1 ? (size_t)(B * (L.T / k) + L.M_cap / k + 1) * 4 : 0;
+  L.off_maps = take(2 * maps + 2 * sk_maps + 64);
   L.total = off;
   return L;
 }
@@ -283,7 +307,7 @@ size_t arena_size(const aenc_geometry* g, int C_pad, size_t esz, int T) {
   int64_t elems = d * 3 * C_pad + d * 3 * d + L * (3 * d * d + d * d + f * d + d * f);
   int64_t floats = 2 * d + L * (2 * d + 3 * d + d + 2 * d + f + d) + 2 * d + (int64_t)T * d;
   if (g->proj_hidden) {
-    elems += (int64_t)g->proj_hidden * d + (int64_t)g->proj_out * g->proj_hidden;
+    elems += (int64_t)g->proj_hidden * stack_of(g) * d + (int64_t)g->proj_out * g->proj_hidden;
     floats += g->proj_hidden + g->proj_out;
   }
   // + 256 B alignment slack per tensor
@@ -336,9 +360,10 @@ bool build(aenc_handle* h, const aenc_weights* w) {
   if (!B.vec(h->lnf_g, w->lnf_g, d, 1.0f) || !B.vec(h->lnf_b, w->lnf_b, d, 0.0f)) return false;
   if (g.proj_hidden) {
     const int ph = g.proj_hidden, po = g.proj_out;
-    h->proj1_w = B.take((size_t)ph * d * esz); h->proj1_b = (float*)B.take(ph * 4);
+    const size_t p1 = (size_t)ph * stack_of(&g) * d * esz;
+    h->proj1_w = B.take(p1); h->proj1_b = (float*)B.take(ph * 4);
     h->proj2_w = B.take((size_t)po * ph * esz); h->proj2_b = (float*)B.take(po * 4);
-    if (!B.copy(h->proj1_w, w->proj1_w, (size_t)ph * d * esz) || !B.vec(h->proj1_b, w->proj1_b, ph, 0.0f) ||
+    if (!B.copy(h->proj1_w, w->proj1_w, p1) || !B.vec(h->proj1_b, w->proj1_b, ph, 0.0f) ||
         !B.copy(h->proj2_w, w->proj2_w, (size_t)po * ph * esz) || !B.vec(h->proj2_b, w->proj2_b, po, 0.0f))
       return false;
   }
@@ -376,6 +401,18 @@ bool build(aenc_handle* h, const aenc_weights* w) {
   h->id_m_valid = maps; maps += 1;
   HIP_TRY(build_row_maps(nullptr, g.batch, h->T, h->id_row_map, h->id_inv_map, h->id_cu, h->id_lens,
                          h->id_m_valid, nullptr));
+  const int k = stack_of(&g);
+  if (k > 1) {
+    const int64_t BTk = (int64_t)g.batch * (h->T / k);
+    h->sk_row_map = maps; maps += BTk;
+    h->sk_inv_map = maps; maps += h->M_cap / k;
+    h->sk_m_valid = maps; maps += 1;
+    h->id_sk_row_map = maps; maps += BTk;
+    h->id_sk_inv_map = maps; maps += h->M_cap / k;
+    h->id_sk_m_valid = maps; maps += 1;
+    HIP_TRY(build_stack_maps(h->id_cu, h->id_lens, g.batch, h->T, k, h->id_sk_row_map, h->id_sk_inv_map,
+                             h->id_sk_m_valid, nullptr));
+  }
   HIP_TRY(hipDeviceSynchronize());
   return true;
 }
@@ -416,7 +453,7 @@ extern "C" aenc_handle* aenc_create(const aenc_geometry* g, const aenc_weights* 
   h->device = dev;
   const Layout Ly = workspace_layout(g);
   h->T = Ly.T; h->T8 = Ly.T8; h->C_pad = Ly.C_pad; h->M_cap = Ly.M_cap; h->ld_vt = Ly.ld_vt; h->esz = Ly.esz;
-  h->launches_per_forward = 7 * g->n_layers + 8;
+  h->launches_per_forward = 7 * g->n_layers + 9;
   if (!build(h, w)) {
     std::string msg = g_last_error;
     release(h);
@@ -534,11 +571,19 @@ extern "C" int aenc_forward(aenc_handle* h, const void* mel, const uint8_t* mask
 
   const int32_t *row_map = h->id_row_map, *inv_map = h->id_inv_map, *cu = h->id_cu, *lens = h->id_lens,
                 *mv = h->id_m_valid;
+  const int k = stack_of(&g);
+  const int32_t *sk_row_map = h->id_sk_row_map, *sk_inv_map = h->id_sk_inv_map, *sk_mv = h->id_sk_m_valid;
   if (mask) {
     if (!q.done(K_MAPS, build_row_maps(mask, B, T, h->row_map, h->inv_map, h->cu, h->lens, h->m_valid, s),
                 "mask maps"))
       return AENC_E_HIP;
     row_map = h->row_map; inv_map = h->inv_map; cu = h->cu; lens = h->lens; mv = h->m_valid;
+    if (k > 1) {
+      if (!q.done(K_MAPS, build_stack_maps(cu, lens, B, T, k, h->sk_row_map, h->sk_inv_map, h->sk_m_valid, s),
+                  "stack maps"))
+        return AENC_E_HIP;
+      sk_row_map = h->sk_row_map; sk_inv_map = h->sk_inv_map; sk_mv = h->sk_m_valid;
+    }
   }
   // Rows of the packed layout the GEMMs must cover at most (all clips full).
   const int M_rows = (int)((int64_t)(B - 1) * h->T8 + T);
@@ -648,26 +693,36 @@ extern "C" int aenc_forward(aenc_handle* h, const void* mel, const uint8_t* mask
   const int ph = g.proj_hidden, po = g.proj_out;
   if (!q.done(K_FINAL, layernorm(h->x, h->lnf_g, h->lnf_b, h->a, g.dtype, M_rows, mv, d, g.ln_eps, s), "final ln"))
     return AENC_E_HIP;
+  // Projector rows: the packed LN rows themselves, or (stack k) runs of k
+  // packed rows read as one k*d-wide row. Clip starts are multiples of 8, so
+  // a run never straddles two clips; stacked row r holds packed rows
+  // k r .. k r + k - 1, all inside the workspace (M_cap is a multiple of 8).
+  const int pin = k * d;
+  const int Mp = k > 1 ? (M_rows + k - 1) / k : M_rows;
+  const int32_t* mvp = k > 1 ? sk_mv : mv;
   EpiParams ep1{};
   ep1.bias = h->proj1_b;
   ep1.c = h->hmid;
   ep1.crow = dense_rows(ph);
-  e = bf ? gemm_bf16(EPI_GELU_BF16, (const bf16_t*)h->a, dense_d, (const bf16_t*)h->proj1_w, d, M_rows, ph, d, mv, ep1,
-                     pick_tile(M_rows, ph), s)
-         : gemm_f32(EPI_GELU_F32, (const float*)h->a, dense_d, (const float*)h->proj1_w, d, M_rows, ph, d, mv, ep1, s);
+  e = bf ? gemm_bf16(EPI_GELU_BF16, (const bf16_t*)h->a, dense_rows(pin), (const bf16_t*)h->proj1_w, pin, Mp, ph,
+                     pin, mvp, ep1, pick_tile(Mp, ph), s)
+         : gemm_f32(EPI_GELU_F32, (const float*)h->a, dense_rows(pin), (const float*)h->proj1_w, pin, Mp, ph, pin, mvp,
+                    ep1, s);
   if (!q.done(K_PROJ1, e, "proj1")) return AENC_E_HIP;
 
   EpiParams ep2{};
   ep2.bias = h->proj2_b;
   ep2.c = out;
-  ep2.crow = RowMap{INT32_MAX, 0, po, 0, inv_map};   // packed row -> b*T + t
+  // packed (or stacked) row -> output row b * T_out + j, or -1 (not written)
+  ep2.crow = RowMap{INT32_MAX, 0, po, 0, k > 1 ? sk_inv_map : inv_map};
   const int epi2 = g.out_dtype == AENC_BF16 ? EPI_STORE_BF16 : EPI_STORE_F32;
-  e = bf ? gemm_bf16(epi2, (const bf16_t*)h->hmid, dense_rows(ph), (const bf16_t*)h->proj2_w, ph, M_rows, po, ph, mv,
-                     ep2, pick_tile(M_rows, po), s)
-         : gemm_f32(epi2, (const float*)h->hmid, dense_rows(ph), (const float*)h->proj2_w, ph, M_rows, po, ph, mv, ep2, s);
+  e = bf ? gemm_bf16(epi2, (const bf16_t*)h->hmid, dense_rows(ph), (const bf16_t*)h->proj2_w, ph, Mp, po, ph, mvp,
+                     ep2, pick_tile(Mp, po), s)
+         : gemm_f32(epi2, (const float*)h->hmid, dense_rows(ph), (const float*)h->proj2_w, ph, Mp, po, ph, mvp, ep2, s);
   if (!q.done(K_PROJ2, e, "proj2")) return AENC_E_HIP;
   if (mask) {
-    if (!q.done(K_ZERO, zero_masked_rows(row_map, out, g.out_dtype, B * T, po, s), "zero masked rows"))
+    const int32_t* zmap = k > 1 ? sk_row_map : row_map;
+    if (!q.done(K_ZERO, zero_masked_rows(zmap, out, g.out_dtype, B * (T / k), po, s), "zero masked rows"))
       return AENC_E_HIP;
   }
   return AENC_OK;

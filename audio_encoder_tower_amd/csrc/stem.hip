@@ -128,6 +128,34 @@ hipError_t build_row_maps(const uint8_t* mask, int B, int T, int32_t* row_map, i
   return hipGetLastError();
 }
 
+// One workgroup: clip by clip, every stacked row of the clip's packed range
+// gets its output row (or -1), and every output row its stacked row (or -1).
+__global__ __launch_bounds__(SCAN_THREADS) void stack_maps_kernel(const int32_t* __restrict__ cu,
+                                                                  const int32_t* __restrict__ lens, int B, int T,
+                                                                  int k, int32_t* __restrict__ row_map,
+                                                                  int32_t* __restrict__ inv_map,
+                                                                  int32_t* __restrict__ m_valid, int inv_cap) {
+  const int tid = threadIdx.x;
+  const int t_out = T / k;
+  for (int b = 0; b < B; ++b) {
+    const int start = cu[b] / k;
+    const int n = min(lens[b] / k, t_out);    // complete runs of k valid positions
+    const int end = b + 1 < B ? cu[b + 1] / k : inv_cap;
+    for (int j = tid; j < t_out; j += SCAN_THREADS) row_map[(int64_t)b * t_out + j] = j < n ? start + j : -1;
+    for (int r = start + tid; r < end; r += SCAN_THREADS) inv_map[r] = r - start < n ? b * t_out + (r - start) : -1;
+  }
+  if (tid == 0) *m_valid = (cu[B] + k - 1) / k;
+}
+
+hipError_t build_stack_maps(const int32_t* cu, const int32_t* lens, int B, int T, int k, int32_t* row_map,
+                            int32_t* inv_map, int32_t* m_valid, hipStream_t stream) {
+  if (k < 1 || 8 % k != 0) return hipErrorInvalidValue;
+  const int inv_cap = B * ((T + 7) & ~7) / k;
+  hipLaunchKernelGGL(stack_maps_kernel, dim3(1), dim3(SCAN_THREADS), 0, stream, cu, lens, B, T, k, row_map, inv_map,
+                     m_valid, inv_cap);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------
 // Weight preparation (at create time only).
 // ---------------------------------------------------------------------------

@@ -33,16 +33,17 @@ PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
 
 
-def step_flops(g, kind: str, rows: int) -> float:
-    """Algorithmic FLOPs of one launch of a GEMM-like step over `rows` valid positions."""
+def step_flops(g, kind: str, rows: int, proj_rows: int) -> float:
+    """Algorithmic FLOPs of one launch of a GEMM-like step over `rows` valid
+    positions (`proj_rows` projector input rows: positions / stack)."""
     d, f = g.d_model, g.d_ffn
     return {
         "qkv": 2.0 * rows * d * 3 * d,
         "o_proj": 2.0 * rows * d * d,
         "fc1": 2.0 * rows * d * f,
         "fc2": 2.0 * rows * f * d,
-        "proj1": 2.0 * rows * d * g.proj_hidden,
-        "proj2": 2.0 * rows * g.proj_hidden * g.proj_out,
+        "proj1": 2.0 * proj_rows * g.proj_in * g.proj_hidden,
+        "proj2": 2.0 * proj_rows * g.proj_hidden * g.proj_out,
     }.get(kind, 0.0)
 
 
@@ -192,12 +193,13 @@ def main():
     enc.profile(False)
 
     rows = int(tb.sum())
+    proj_rows = int((tb // g.stack).sum())
     per_kind = {}
     for k, (ms, n) in sorted(kinds.items(), key=lambda kv: -kv[1][0]):
         avg = ms / n
         entry = {"ms_per_step": round(ms / args.steps, 4), "launches_per_step": n // args.steps,
                  "avg_launch_ms": round(avg, 5)}
-        fl = step_flops(g, k, rows) if k != "attention" else attention_flops(g, tb)
+        fl = step_flops(g, k, rows, proj_rows) if k != "attention" else attention_flops(g, tb)
         if fl:
             entry["tflops"] = round(fl / (avg * 1e-3) / 1e12, 1)
         if k == "layernorm":   # fp32 rows in, bf16 (or fp32) rows out
@@ -207,7 +209,7 @@ def main():
     dominant = max(kinds, key=lambda k: kinds[k][0])
     dom_ms, dom_n = kinds[dominant]
     dom_avg = dom_ms / dom_n
-    dom_flops = step_flops(g, dominant, rows) if dominant != "attention" else attention_flops(g, tb)
+    dom_flops = step_flops(g, dominant, rows, proj_rows) if dominant != "attention" else attention_flops(g, tb)
     peak = PEAK_TFLOPS[g.dtype]
     roofline = {
         "kernel": dominant,
@@ -237,7 +239,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "global_batch": g.batch, "seq_len": g.n_pos, "mel_frames": g.n_frames,
                    "d_model": g.d_model, "layers": g.n_layers, "heads": g.n_heads, "ffn": g.d_ffn,
-                   "pool_step": g.pool_step, "projector": [g.proj_hidden, g.proj_out] if g.proj_hidden else None,
+                   "pool_step": g.pool_step, "stack": g.stack,
+                   "projector": [g.proj_in, g.proj_hidden, g.proj_out] if g.proj_hidden else None,
                    "audio_seconds_per_step": audio_s, "parallelism": "none (1 GPU)"},
         "tflops": round(tflops, 1),
         "mfma_frac": round(tflops / peak, 4),

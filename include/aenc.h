@@ -76,6 +76,13 @@ typedef struct aenc_geometry {
   int32_t dtype;        /* AENC_BF16 (fp32 accumulate, fp32 residual) or AENC_F32           */
   int32_t out_dtype;    /* element type of `out`: AENC_F32 or AENC_BF16                       */
   float ln_eps;         /* LayerNorm epsilon (> 0), e.g. 1e-5                                */
+  int32_t stack;        /* 0 or 1: none. 4: the projector reads runs of 4 consecutive final-LN
+                         * positions concatenated in order ([T, d] -> [T/4, 4d], a trailing
+                         * partial run dropped), i.e. 12.5 rows per second of audio with a
+                         * 4d-wide projector input (Whisper features downsampled to 12.5 Hz,
+                         * "[WIP][TSS][Model] Kimi-Audio-7B", Purpose; kimia_adaptor_input_dim
+                         * 5120, "Kimi-Audio-7B-Instruct", (1) AUDIO). Needs a projector and
+                         * pool_step 1.                                                    */
 } aenc_geometry;
 
 /* One block's tensors (d = d_model, f = d_ffn). Pointers may be host or device
@@ -97,7 +104,7 @@ typedef struct aenc_weights {
   const void *conv2_w, *conv2_b;        /* [d, d, 3], [d]            */
   const aenc_layer_weights *layers;     /* host array of n_layers    */
   const void *lnf_g, *lnf_b;            /* [d]                       */
-  const void *proj1_w, *proj1_b;        /* [proj_hidden, d], [proj_hidden]        (projector only) */
+  const void *proj1_w, *proj1_b;        /* [proj_hidden, stack*d], [proj_hidden]  (projector only) */
   const void *proj2_w, *proj2_b;        /* [proj_out, proj_hidden], [proj_out]    (projector only) */
 } aenc_weights;
 

@@ -112,6 +112,7 @@ FULL_SIZE_SAMPLES = {
     "whisper_medium_pool2_b1": dict(clips=[0], every=1),
     "whisper_large_b1": dict(clips=[0], every=1),
     "whisper_large_proj_b16": dict(clips=[0, 15], every=5),
+    "whisper_large_stack4_proj_b16": dict(clips=[0, 15], every=3),
     "whisper_large_varlen_b32": dict(clips=None, every=5),   # shortest, longest and one in between
 }
 

@@ -70,6 +70,8 @@ BAD = {
     "eps0": dict(ln_eps=0.0),
     "eps_nan": dict(ln_eps=float("nan")),
     "neg_layers": dict(n_layers=-1),
+    "stack3": dict(stack=3, proj_hidden=128, proj_out=128),
+    "stack4_too_short": dict(stack=4, proj_hidden=128, proj_out=128, n_frames=6),
 }
 
 
@@ -91,6 +93,26 @@ def test_pool_with_projector_is_unsupported(aenc):
     g = synth.get_workload("whisper_medium_pool2_b1").geom.replace(proj_hidden=128, proj_out=128)
     assert aenc.validate(g) == -2
     assert "pool" in aenc.last_error()
+
+
+def test_stacking_needs_a_projector(aenc):
+    g = synth.get_workload("whisper_large_b1").geom.replace(stack=4)
+    assert aenc.validate(g) == -2
+    assert "projector" in aenc.last_error()
+    g = synth.get_workload("whisper_medium_pool2_b1").geom.replace(stack=4, proj_hidden=128, proj_out=128)
+    assert aenc.validate(g) == -2
+
+
+def test_stacked_geometry_counts(aenc):
+    """stack 4: 375 output rows per 30 s clip and a 4 d-wide projector input,
+    the same closed forms on both sides of the boundary."""
+    g = synth.get_workload("whisper_large_stack4_proj_b16").geom
+    assert aenc.output_shape(g) == (16, 375, 3072)
+    assert aenc.param_count(g) - aenc.param_count(g.replace(stack=1)) == 3 * 1280 * 3072
+    # a zero stack field (a caller that predates it) means no stacking
+    gg = aenc._lib.geometry(g.replace(stack=1))
+    gg.stack = 0
+    assert aenc.lib().aenc_validate(ctypes.byref(gg)) == 0
 
 
 def test_null_arguments(aenc):

@@ -85,6 +85,16 @@ REDUCED = {
     "fp32_perturbed_masked": reduced("tiny_fp32_b1", "fp32_perturbed_masked", dict(batch=3), init="perturbed"),
     "fp32_projector": reduced("tiny_fp32_b1", "fp32_projector", dict(proj_hidden=128, proj_out=192),
                               init="perturbed"),
+    # 4 positions stacked into the projector input, key mask over 3 clips
+    "stack4_masked": reduced("whisper_large_b1", "stack4_masked",
+                             dict(batch=3, n_layers=1, n_frames=900, d_model=256, n_heads=4, d_ffn=1024,
+                                  proj_hidden=512, proj_out=384, stack=4), init="perturbed"),
+    # Whisper-large width, stacked 5120-wide projector input, 2 clips of 500 positions
+    "stack4_large_width": reduced("whisper_large_b1", "stack4_large_width",
+                                  dict(batch=2, n_layers=1, n_frames=1000, proj_hidden=3072, proj_out=3072,
+                                       stack=4), init="perturbed"),
+    "fp32_stack4": reduced("tiny_fp32_b1", "fp32_stack4", dict(proj_hidden=128, proj_out=192, stack=4, batch=2),
+                           init="perturbed"),
 }
 
 
@@ -93,6 +103,8 @@ REDUCED = {
 LENGTHS = {
     "projector_masked": [900, 411, 101],
     "fp32_perturbed_masked": [200, 137, 61],
+    "stack4_masked": [900, 411, 101],
+    "fp32_stack4": [200, 117],
 }
 
 
@@ -111,8 +123,9 @@ def compare(w, got, ref, mask, what):
     g = w.geom
     rows = np.ones(got.shape[:2], bool)
     if mask is not None:
-        t_out = g.t_out
-        valid = mask[:, : t_out * g.pool_step].reshape(mask.shape[0], t_out, g.pool_step).all(-1)
+        # an output row is defined when every position it reads is valid
+        t_out, span = g.t_out, g.pool_step * g.stack
+        valid = mask[:, : t_out * span].reshape(mask.shape[0], t_out, span).all(-1)
         rows = valid
         # masked rows are written as zeros
         assert np.all(got[~rows] == 0.0), f"{what}: masked rows not zero"
