@@ -17,7 +17,13 @@
 //   - P^T in registers is exactly the B operand of O^T = V^T P^T, so P never
 //     goes through LDS; V^T's keys are stored in the order that matches;
 //   - scores are scaled by 1/sqrt(64) and turned into base-2 exponents in a
-//     single fma; softmax statistics and the output accumulate in fp32.
+//     single fma; softmax statistics and the output accumulate in fp32;
+//   - the running maximum is moved (and the sums rescaled) only when a row's
+//     tile maximum exceeds it by more than 2^8 in probability: until then the
+//     stale maximum only scales every term of the row by the same factor
+//     (at most 256), which the final division by the row sum cancels. With
+//     32 queries per wave, an exact running maximum would rescale on most
+//     tiles.
 #include <type_traits>
 
 #include "common.h"
@@ -67,16 +73,27 @@ __global__ __launch_bounds__(256) void attention_bf16_kernel(const bf16_t* __res
   // RAGGED: the tile may run past the clip; key rows are clamped and the
   // values of keys past the clip are zeroed (a zero probability times a
   // non-finite value would still poison the sum).
+  // Per-lane chunk pointers for k0 = 0; a tile adds the uniform k0 offsets.
+  const bf16_t* kp[2];
+  const bf16_t* vp[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = tid + 256 * i;
+    kp[i] = kbase + (int64_t)(start + (c >> 3)) * ld_qk + (c & 7) * 8;
+    vp[i] = vbase + (int64_t)(c >> 3) * ld_vt + (c & 7) * 8;
+  }
   auto gload = [&](int k0, auto ragged) {
     constexpr bool RAGGED = decltype(ragged)::value;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int c = tid + 256 * i;
       const int key = c >> 3, ch = c & 7;
-      const int krow = RAGGED ? min(k0 + key, len - 1) : k0 + key;
-      rk[i] = *(const u32x4*)(kbase + (int64_t)(start + krow) * ld_qk + ch * 8);
-      const int e = c >> 3, kc = c & 7;
-      u32x4 v = *(const u32x4*)(vbase + (int64_t)e * ld_vt + k0 + kc * 8);
+      if (RAGGED)
+        rk[i] = *(const u32x4*)(kbase + (int64_t)(start + min(k0 + key, len - 1)) * ld_qk + ch * 8);
+      else
+        rk[i] = *(const u32x4*)(kp[i] + (int64_t)k0 * ld_qk);
+      const int kc = c & 7;
+      u32x4 v = *(const u32x4*)(vp[i] + k0);
       if (RAGGED) {
         const int first = k0 + kc * 8;
 #pragma unroll
@@ -110,6 +127,7 @@ __global__ __launch_bounds__(256) void attention_bf16_kernel(const bf16_t* __res
   };
 
   const float c = 0.125f * 1.44269504088896341f;           // 1/sqrt(64) * log2(e)
+  const float slack = 8.0f / c;                              // 2^8 headroom, in score units
   float m_run = -INFINITY, l_run = 0.0f;
   f32x16 oacc[2];
 #pragma unroll
@@ -148,9 +166,9 @@ __global__ __launch_bounds__(256) void attention_bf16_kernel(const bf16_t* __res
 #pragma unroll
       for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[sub][v]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    // Rescale the running sums only when some row's maximum grew (a uniform
-    // branch: after the first tiles the maximum rarely moves).
-    if (__any(mx > m_run)) {
+    // Rescale only when some row's maximum outgrew the reference by more than
+    // the slack (a uniform branch, rarely taken after the first tile).
+    if (__any(mx > m_run + slack)) {
       const float m_new = fmaxf(m_run, mx);
       const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
       m_run = m_new;
