@@ -87,7 +87,7 @@ struct Epilogue {
     if (EPI == EPI_STORE_BF16 || EPI == EPI_QKV_BF16) {
       ((bf16_t*)p.c)[o + n] = f32_to_bf16(x);
     } else if (EPI == EPI_GELU_BF16) {
-      ((bf16_t*)p.c)[o + n] = f32_to_bf16(gelu_erf(x));
+      ((bf16_t*)p.c)[o + n] = f32_to_bf16(gelu_bf16out(x));
     } else if (EPI == EPI_RESID_F32) {
       float* dst = (float*)p.c + o + n;
       *dst = *dst + x;
@@ -182,7 +182,10 @@ struct Epilogue {
         v.x = gelu_erf(v.x) + pe.x; v.y = gelu_erf(v.y) + pe.y;
         v.z = gelu_erf(v.z) + pe.z; v.w = gelu_erf(v.w) + pe.w;
       }
-      if (EPI == EPI_GELU_BF16 || EPI == EPI_GELU_F32) {
+      if (EPI == EPI_GELU_BF16) {
+        v.x = gelu_bf16out(v.x); v.y = gelu_bf16out(v.y); v.z = gelu_bf16out(v.z); v.w = gelu_bf16out(v.w);
+      }
+      if (EPI == EPI_GELU_F32) {
         v.x = gelu_erf(v.x); v.y = gelu_erf(v.y); v.z = gelu_erf(v.z); v.w = gelu_erf(v.w);
       }
       off[it] = o;
