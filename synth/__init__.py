@@ -6,6 +6,6 @@ encoder's arithmetic lives here.
 """
 from .workloads import Geometry, Workload, WORKLOADS, get_workload  # noqa: F401
 from .inputs import (  # noqa: F401
-    weight_shapes, make_weights, make_mel, make_lengths, make_mask,
+    weight_shapes, make_weights, make_mel, make_lengths, make_mask, make_audio,
     to_bf16_bits, bf16_bits_to_f32, round_to_bf16,
 )

@@ -158,6 +158,34 @@ def make_mel(w: Workload, clips=None) -> np.ndarray:
     return out
 
 
+def make_audio(seed: int, clips: int, n_samples: int = 480000, sample_rate: int = 16000) -> np.ndarray:
+    """Seeded synthetic 16 kHz waveforms [clips, n_samples] float32 in [-1, 1].
+
+    Speech-like stand-ins (no audio data is available): per clip a few
+    harmonic tone stacks with drifting pitch and a syllable-rate amplitude
+    envelope, plus low-level noise and short silent gaps, so the spectra
+    have both peaks and an 80 dB-deep floor. Clip i draws stream (seed, i).
+    """
+    t = np.arange(n_samples, dtype=np.float64) / sample_rate
+    out = np.empty((clips, n_samples), np.float32)
+    for i in range(clips):
+        rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed, spawn_key=(int(i),))))
+        x = np.zeros(n_samples)
+        for _ in range(3):
+            f0 = rng.uniform(90.0, 260.0)
+            drift = rng.uniform(-0.3, 0.3) * np.sin(2 * np.pi * rng.uniform(0.1, 0.5) * t)
+            phase = 2 * np.pi * np.cumsum(f0 * (1.0 + 0.1 * drift)) / sample_rate
+            for h in range(1, 12):
+                x += rng.uniform(0.2, 1.0) / h * np.sin(h * phase + rng.uniform(0, 2 * np.pi))
+        env = 0.5 + 0.5 * np.sin(2 * np.pi * rng.uniform(2.0, 6.0) * t + rng.uniform(0, 2 * np.pi))
+        x = x * env ** 2 + 0.02 * rng.standard_normal(n_samples)
+        for _ in range(4):                        # silent gaps
+            a = int(rng.integers(0, n_samples - 8000))
+            x[a:a + int(rng.integers(1600, 8000))] *= 1e-4
+        out[i] = (0.9 * x / np.abs(x).max()).astype(np.float32)
+    return out
+
+
 def make_mask(w: Workload, clips=None):
     """Key-padding mask uint8 [len(clips), T] (1 = valid), or None if all valid.
 
