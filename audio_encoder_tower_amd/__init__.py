@@ -5,4 +5,5 @@ of include/aenc.h (libaenc.so); this package is its Python binding.
 """
 from ._lib import AencError, AENC_BF16, AENC_F32, lib, last_error  # noqa: F401
 from .encoder import Encoder, output_shape, param_count, validate  # noqa: F401
+from .frontend import Frontend, frontend_output_shape  # noqa: F401
 from . import steps  # noqa: F401

@@ -40,6 +40,10 @@ class Weights(ctypes.Structure):
                 ("proj1_w", c_void_p), ("proj1_b", c_void_p), ("proj2_w", c_void_p), ("proj2_b", c_void_p)]
 
 
+class FrontendConfig(ctypes.Structure):
+    _fields_ = [("batch", c_int32), ("n_samples", c_int32), ("n_mel", c_int32), ("out_dtype", c_int32)]
+
+
 class AencError(RuntimeError):
     pass
 
@@ -71,6 +75,11 @@ SIGNATURES = {
     "aenc_k_row_maps": (c_int, [c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                 c_void_p]),
     "aenc_k_copy": (c_int, [c_void_p, c_void_p, c_int64, c_void_p]),
+    # front end (aenc.h)
+    "aenc_frontend_output_shape": (c_int, [POINTER(FrontendConfig), POINTER(c_int64)]),
+    "aenc_frontend_create": (c_void_p, [POINTER(FrontendConfig)]),
+    "aenc_frontend_run": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p]),
+    "aenc_frontend_destroy": (None, [c_void_p]),
 }
 
 

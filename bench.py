@@ -119,6 +119,32 @@ def measured_traffic(kind: str):
     return entry.get("bytes_per_launch")
 
 
+def frontend_leg(batch: int, steps: int):
+    """Time the GPU log-mel front end on `batch` 30 s clips (audio resident in HBM)."""
+    import torch
+    import audio_encoder_tower_amd as aenc
+    n = 480000
+    audio = torch.from_numpy(synth.make_audio(5, batch, n)).cuda()
+    fe = aenc.Frontend(batch, n, 128, out_dtype="bf16")
+    out = fe(audio)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        fe(audio, out)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    fe.close()
+    frames = batch * (n // 160)
+    dft_flops = 2.0 * frames * 404 * 400
+    mel_flops = 2.0 * frames * 128 * 208
+    return {"workload": f"{batch} clips of 30 s, 16 kHz -> [{batch}, 128, 3000] bf16", "ms_per_batch": round(ms, 4),
+            "audio_s_per_s": round(batch * 30.0 / (ms * 1e-3), 1),
+            "fp32_tflops": round((dft_flops + mel_flops) / (ms * 1e-3) / 1e12, 2)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -127,6 +153,7 @@ def main():
     ap.add_argument("--workload", default=synth.workloads.HEADLINE)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-blocks", type=int, default=0, help="blocks the CPU oracle runs (0: all)")
+    ap.add_argument("--no-frontend", action="store_true", help="skip timing the log-mel front end")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run the plain copy kernel over this many MiB (a reference for traffic counters)")
     args = ap.parse_args()
@@ -249,6 +276,8 @@ def main():
         "roofline": roofline,
         "kernels": per_kind,
     }
+    if not args.no_frontend:
+        result["frontend"] = frontend_leg(g.batch, args.steps)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_blocks)
     print(json.dumps(result), flush=True)

@@ -169,6 +169,44 @@ int aenc_profile_read(aenc_handle *h, double *ms, int64_t *calls, int n_kinds);
 int aenc_profile_kind_count(void);
 const char *aenc_profile_kind_name(int kind);
 
+/* ---------------------------------------------------------------------------
+ * Log-mel front end: 16 kHz audio -> the encoder's input features.
+ *
+ * The extractor's geometry is the pages' Whisper feature extractor (16 kHz,
+ * 480,000 samples per 30 s chunk, n_fft 400, hop 160, 128 features, 3000
+ * frames: "Voxtral-Mini-3B-2507", Preprocessor). Its steps follow the Whisper
+ * recipe: centred frames with reflect padding of 200 samples, periodic Hann
+ * window, power spectrum of bins 0..200 with the last centred frame dropped,
+ * Slaney-scale triangular mel filters of unit area (0 to 8 kHz), log10
+ * floored at 1e-10, then floored at the clip's maximum minus 8, then
+ * (x + 4) / 4.
+ * ------------------------------------------------------------------------- */
+typedef struct aenc_frontend_config {
+  int32_t batch;        /* clips per call; the workspace is sized for it            */
+  int32_t n_samples;    /* samples per clip: a multiple of 160, above 200 (480000) */
+  int32_t n_mel;        /* filters (1 .. 512): 128 or 80                             */
+  int32_t out_dtype;    /* AENC_F32 or AENC_BF16                                     */
+} aenc_frontend_config;
+
+typedef struct aenc_frontend aenc_frontend;
+
+/* [batch, n_mel, n_samples / 160]: the frame count is the hop count (3000 for
+ * 480,000 samples). Validates the config (AENC_E_INVAL when it is bad). */
+int aenc_frontend_output_shape(const aenc_frontend_config *c, int64_t shape[3]);
+
+/* Build the DFT matrix and the filters on the current device and allocate the
+ * workspace (about 4 * batch * n_samples * 8 bytes). NULL on error. */
+aenc_frontend *aenc_frontend_create(const aenc_frontend_config *c);
+
+/* audio: device fp32 [batch, n_samples]; mel: device [batch, n_mel, frames]
+ * in out_dtype, channels first (the layout aenc_forward reads). Enqueues on
+ * `stream` without synchronising and allocates nothing. Calls on one handle
+ * must be stream-ordered (one workspace). */
+int aenc_frontend_run(aenc_frontend *h, const float *audio, void *mel, void *stream);
+
+/* Free the handle (NULL is accepted). */
+void aenc_frontend_destroy(aenc_frontend *h);
+
 #ifdef __cplusplus
 }
 #endif

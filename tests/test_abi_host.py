@@ -115,6 +115,20 @@ def test_stacked_geometry_counts(aenc):
     assert aenc.lib().aenc_validate(ctypes.byref(gg)) == 0
 
 
+def test_frontend_shapes_and_configs(aenc):
+    assert aenc.frontend_output_shape(16, 480000, 128) == (16, 128, 3000)     # 30 s -> 3000 frames
+    assert aenc.frontend_output_shape(2, 80000, 80, "f32") == (2, 80, 500)
+    for bad in (dict(batch=0), dict(n_samples=1000), dict(n_samples=160), dict(n_mel=0), dict(n_mel=600)):
+        kw = dict(batch=1, n_samples=16000, n_mel=128)
+        kw.update(bad)
+        with pytest.raises(aenc.AencError):
+            aenc.frontend_output_shape(**kw)
+    L = aenc.lib()
+    assert L.aenc_frontend_create(None) is None
+    assert L.aenc_frontend_run(None, None, None, None) == -1
+    L.aenc_frontend_destroy(None)
+
+
 def test_null_arguments(aenc):
     L = aenc.lib()
     assert L.aenc_validate(None) == -1
