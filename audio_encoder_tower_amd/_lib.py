@@ -75,6 +75,16 @@ SIGNATURES = {
     "aenc_k_row_maps": (c_int, [c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                 c_void_p]),
     "aenc_k_copy": (c_int, [c_void_p, c_void_p, c_int64, c_void_p]),
+    "aenc_handle_geometry": (c_int, [c_void_p, POINTER(Geometry)]),
+    # embeddings cache (aenc.h)
+    "aenc_cache_create": (c_void_p, [c_int64, c_int64]),
+    "aenc_cache_destroy": (None, [c_void_p]),
+    "aenc_cache_contains": (c_int, [c_void_p, ctypes.c_uint64]),
+    "aenc_cache_lookup": (c_int, [c_void_p, ctypes.c_uint64, c_void_p, c_void_p]),
+    "aenc_cache_insert": (c_int, [c_void_p, ctypes.c_uint64, c_void_p, c_void_p]),
+    "aenc_cache_stats": (c_int, [c_void_p, POINTER(c_int64)]),
+    "aenc_forward_cached": (c_int, [c_void_p, c_void_p, POINTER(ctypes.c_uint64), c_void_p, c_void_p, c_void_p,
+                                    c_void_p, POINTER(ctypes.c_int32)]),
     # front end (aenc.h)
     "aenc_frontend_output_shape": (c_int, [POINTER(FrontendConfig), POINTER(c_int64)]),
     "aenc_frontend_create": (c_void_p, [POINTER(FrontendConfig)]),

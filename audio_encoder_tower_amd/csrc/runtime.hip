@@ -559,6 +559,12 @@ int pick_tile(int M, int N) { return gemm_pick_tile(M, N); }
 
 }  // namespace
 
+extern "C" int aenc_handle_geometry(const aenc_handle* h, aenc_geometry* g) {
+  if (!h || !g) { set_error("handle and geometry must not be NULL"); return AENC_E_INVAL; }
+  *g = h->g;
+  return AENC_OK;
+}
+
 extern "C" int aenc_forward(aenc_handle* h, const void* mel, const uint8_t* mask, void* out, void* stream) {
   if (!h) { set_error("handle is NULL"); return AENC_E_INVAL; }
   if (!mel || !out) { set_error("mel and out must not be NULL"); return AENC_E_INVAL; }

@@ -115,6 +115,20 @@ class Encoder:
 
     __call__ = forward
 
+    def forward_cached(self, cache: "EmbeddingsCache", keys, mel: torch.Tensor, mask: Optional[torch.Tensor] = None,
+                       out: Optional[torch.Tensor] = None, stream=None):
+        """aenc_forward_cached: returns (out, number of clips served from the cache)."""
+        g = self._g
+        if len(keys) != g.batch:
+            raise ValueError(f"need {g.batch} keys")
+        if out is None:
+            out = torch.empty(self.out_shape, dtype=self.out_dtype, device=mel.device)
+        karr = (ctypes.c_uint64 * g.batch)(*[int(k) & 0xFFFFFFFFFFFFFFFF for k in keys])
+        hits = ctypes.c_int32(0)
+        check(lib().aenc_forward_cached(self._h, cache._c, karr, _ptr(mel), _ptr(mask), _ptr(out),
+                                        _stream_handle(stream), ctypes.byref(hits)), "aenc_forward_cached")
+        return out, int(hits.value)
+
     # -- per-step timing -------------------------------------------------
     def profile(self, on: bool = True) -> None:
         check(lib().aenc_profile_enable(self._h, int(on)), "aenc_profile_enable")
@@ -133,6 +147,51 @@ class Encoder:
         if getattr(self, "_h", None):
             lib().aenc_destroy(self._h)
             self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class EmbeddingsCache:
+    """Device-resident LRU of encoder outputs under 64-bit content keys (aenc_cache_*)."""
+
+    def __init__(self, entry_bytes: int, capacity: int):
+        c = lib().aenc_cache_create(int(entry_bytes), int(capacity))
+        if not c:
+            raise AencError(f"aenc_cache_create: {_lib.last_error()}")
+        self._c = ctypes.c_void_p(c)
+        self.entry_bytes = int(entry_bytes)
+
+    @classmethod
+    def for_encoder(cls, enc: "Encoder", capacity: int) -> "EmbeddingsCache":
+        per_clip = enc.out_shape[1] * enc.out_shape[2] * (2 if enc.out_dtype == torch.bfloat16 else 4)
+        return cls(per_clip, capacity)
+
+    def __contains__(self, key) -> bool:
+        return lib().aenc_cache_contains(self._c, int(key) & 0xFFFFFFFFFFFFFFFF) == 1
+
+    def lookup(self, key, dst: torch.Tensor, stream=None) -> bool:
+        st = lib().aenc_cache_lookup(self._c, int(key) & 0xFFFFFFFFFFFFFFFF, _ptr(dst), _stream_handle(stream))
+        if st < 0:
+            check(st, "aenc_cache_lookup")
+        return st == 1
+
+    def insert(self, key, src: torch.Tensor, stream=None) -> None:
+        check(lib().aenc_cache_insert(self._c, int(key) & 0xFFFFFFFFFFFFFFFF, _ptr(src), _stream_handle(stream)),
+              "aenc_cache_insert")
+
+    def stats(self) -> Dict[str, int]:
+        out = (ctypes.c_int64 * 5)()
+        check(lib().aenc_cache_stats(self._c, out), "aenc_cache_stats")
+        return dict(zip(("hits", "misses", "inserts", "evictions", "entries"), (int(v) for v in out)))
+
+    def close(self):
+        if getattr(self, "_c", None):
+            lib().aenc_cache_destroy(self._c)
+            self._c = None
 
     def __del__(self):
         try:

@@ -169,6 +169,46 @@ int aenc_profile_read(aenc_handle *h, double *ms, int64_t *calls, int n_kinds);
 int aenc_profile_kind_count(void);
 const char *aenc_profile_kind_name(int kind);
 
+/* The geometry a handle was created with (NULL arguments: AENC_E_INVAL). */
+int aenc_handle_geometry(const aenc_handle *h, aenc_geometry *g);
+
+/* ---------------------------------------------------------------------------
+ * Embeddings cache: encoder outputs kept on the device under caller-given
+ * 64-bit content keys (for instance a hash of the clip's audio and length),
+ * so a clip seen before is served by a device copy. Serving stacks pair such
+ * a cache with a separately scheduled encoder (TRT-LLM's "Multimodal
+ * Embeddings Cache" and "Multimodal Encoder Side Stream", cited by the
+ * "Kimi-Audio-7B-Instruct" and "Qwen2-Audio-7B-Instruct" records, (1) under
+ * SERVICEABILITY JOIN).
+ *
+ * The pool of `capacity` slots of `entry_bytes` each is allocated at create;
+ * lookups and inserts allocate nothing and enqueue device-to-device copies on
+ * the given stream, ordered after any earlier copy of the same slot (on any
+ * stream). Least recently used slots are recycled. Host calls may come from
+ * several threads.
+ * ------------------------------------------------------------------------- */
+typedef struct aenc_cache aenc_cache;
+
+aenc_cache *aenc_cache_create(int64_t entry_bytes, int64_t capacity);   /* NULL on error */
+void aenc_cache_destroy(aenc_cache *c);                                 /* NULL-safe */
+/* 1 if `key` is cached, else 0 (no copy, no statistics). */
+int aenc_cache_contains(aenc_cache *c, uint64_t key);
+/* Hit: enqueue a copy of the entry into device `dst` (entry_bytes), return 1.
+ * Miss: return 0 and enqueue nothing. */
+int aenc_cache_lookup(aenc_cache *c, uint64_t key, void *dst, void *stream);
+/* Store entry_bytes from device `src` under `key` (replacing its entry, or
+ * taking a free or the least recently used slot). AENC_OK or an error. */
+int aenc_cache_insert(aenc_cache *c, uint64_t key, const void *src, void *stream);
+/* out = {hits, misses, inserts, evictions, entries}. */
+int aenc_cache_stats(aenc_cache *c, int64_t out[5]);
+/* aenc_forward through the cache: keys[b] names clip b (entry_bytes must be
+ * one clip's output, T_out * D_out * element size). If every clip is cached,
+ * only copies are enqueued; otherwise the whole batch runs (its shape is
+ * fixed) and the new clips are stored. *hits (if not NULL) receives the
+ * number of clips found. */
+int aenc_forward_cached(aenc_handle *h, aenc_cache *c, const uint64_t *keys, const void *mel,
+                        const uint8_t *mask, void *out, void *stream, int32_t *hits);
+
 /* ---------------------------------------------------------------------------
  * Log-mel front end: 16 kHz audio -> the encoder's input features.
  *
