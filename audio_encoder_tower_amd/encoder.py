@@ -170,6 +170,28 @@ class EmbeddingsCache:
         per_clip = enc.out_shape[1] * enc.out_shape[2] * (2 if enc.out_dtype == torch.bfloat16 else 4)
         return cls(per_clip, capacity)
 
+    @staticmethod
+    def key_of(data) -> int:
+        """A 64-bit content key: BLAKE2b (8-byte digest) of the raw bytes of
+        `data` (bytes, a NumPy array or a host tensor), with its shape and dtype
+        folded in so that equal bytes of different layouts do not collide."""
+        import hashlib
+        h = hashlib.blake2b(digest_size=8)
+        if isinstance(data, torch.Tensor):
+            if data.is_cuda:
+                raise ValueError("key_of hashes host data: hash the clip before it is copied to the device")
+            t = data.contiguous()
+            arr = (t.view(torch.int16) if t.dtype == torch.bfloat16 else t).numpy()
+            tag = "bfloat16" if t.dtype == torch.bfloat16 else str(arr.dtype)
+            h.update(f"{tag}{tuple(arr.shape)}".encode())
+            h.update(arr.tobytes())
+        elif hasattr(data, "tobytes"):
+            h.update(f"{data.dtype}{tuple(data.shape)}".encode())
+            h.update(data.tobytes())
+        else:
+            h.update(bytes(data))
+        return int.from_bytes(h.digest(), "little")
+
     def __contains__(self, key) -> bool:
         return lib().aenc_cache_contains(self._c, int(key) & 0xFFFFFFFFFFFFFFFF) == 1
 

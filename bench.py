@@ -145,6 +145,92 @@ def frontend_leg(batch: int, steps: int):
             "fp32_tflops": round((dft_flops + mel_flops) / (ms * 1e-3) / 1e12, 2)}
 
 
+def side_stream_leg(enc, mel, mask, out, audio_s: float, n_enc: int = 4, gate_forwards: int = 3, shape=None,
+                    enc_stream=None, dec_stream=None):
+    """The encoder on a stream of its own while a decode-like load (synth.decode_load)
+    runs on another, against each alone.
+
+    Every run starts behind a gate: `gate_forwards` encoder forwards on a third
+    stream, after which an event releases the measured streams; the host
+    enqueues all measured work while the gate holds, so the times are the
+    GPU's and not the host's launch rate. The decode side takes as many steps
+    as last about as long as the encoder's `n_enc` forwards alone.
+    overlap_efficiency = (serial - concurrent) / (serial - max(alone)): 1 when
+    both finish as if each had the GPU to itself, 0 when no better than
+    running one after the other."""
+    import torch
+    from synth.decode_load import DecodeLoad, KIMI_AUDIO_LLM
+    shape = shape or KIMI_AUDIO_LLM
+    load = DecodeLoad(shape)
+    sa = enc_stream or torch.cuda.Stream()
+    sb = dec_stream or torch.cuda.Stream()
+    sg = torch.cuda.Stream()
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    def dec(n):
+        with torch.cuda.stream(sb):
+            for _ in range(n):
+                load.step()
+
+    def gated(streams, enqueue):
+        torch.cuda.synchronize()
+        for _ in range(gate_forwards):
+            enc.forward(mel, mask, out, sg)
+        g0 = ev()
+        g0.record(sg)
+        for s in streams:
+            s.wait_event(g0)
+        t0 = time.perf_counter()
+        enqueue()
+        host_ms = (time.perf_counter() - t0) * 1e3
+        ends = []
+        for s in streams:
+            e = ev()
+            e.record(s)
+            ends.append(e)
+        torch.cuda.synchronize()
+        return [g0.elapsed_time(e) for e in ends], host_ms
+
+    dec(2)                                               # library warm-up
+    enc.forward(mel, mask, out, sa)
+    (t3,), _ = gated([sb], lambda: dec(3))
+    t_step = t3 / 3
+    (t_enc,), _ = gated([sa], lambda: [enc.forward(mel, mask, out, sa) for _ in range(n_enc)])
+    n_dec = max(1, round(t_enc / t_step))
+    (t_dec,), _ = gated([sb], lambda: dec(n_dec))
+
+    def both():
+        done = 0
+        for i in range(n_enc):
+            enc.forward(mel, mask, out, sa)
+            k = round(n_dec * (i + 1) / n_enc) - done
+            dec(k)
+            done += k
+
+    (ta, tb), host_ms = gated([sa, sb], both)
+    t_both = max(ta, tb)
+    serial, ideal = t_enc + t_dec, max(t_enc, t_dec)
+    del load
+    torch.cuda.synchronize()
+    return {
+        "load": f"decode of {shape.tokens} rows through {shape.layers} layers (hidden {shape.hidden}, kv "
+                f"{shape.kv_dim}, intermediate {shape.inter}): {shape.weight_bytes() / 1e9:.2f} GB of bf16 weights "
+                f"per step",
+        "encoder_forwards": n_enc, "decode_steps": n_dec,
+        "encoder_alone_ms": round(t_enc, 3), "decode_alone_ms": round(t_dec, 3),
+        "decode_step_alone_ms": round(t_dec / n_dec, 4),
+        "decode_alone_gbs": round(shape.weight_bytes() * n_dec / (t_dec * 1e-3) / 1e9, 1),
+        "concurrent_ms": round(t_both, 3), "encoder_done_ms": round(ta, 3), "decode_done_ms": round(tb, 3),
+        "encoder_audio_s_per_s_under_load": round(audio_s * n_enc / (ta * 1e-3), 1),
+        "speedup_vs_serial": round(serial / t_both, 4),
+        "overlap_efficiency": round((serial - t_both) / (serial - ideal), 4) if serial > ideal else None,
+        "host_enqueue_ms": round(host_ms, 2),
+        "gate_ms_alone": round(t_enc / n_enc * gate_forwards, 2),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -154,6 +240,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-blocks", type=int, default=0, help="blocks the CPU oracle runs (0: all)")
     ap.add_argument("--no-frontend", action="store_true", help="skip timing the log-mel front end")
+    ap.add_argument("--no-side-stream", action="store_true",
+                    help="skip the encoder-beside-decode overlap measurement")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run the plain copy kernel over this many MiB (a reference for traffic counters)")
     args = ap.parse_args()
@@ -278,6 +366,8 @@ def main():
     }
     if not args.no_frontend:
         result["frontend"] = frontend_leg(g.batch, args.steps)
+    if not args.no_side_stream:
+        result["side_stream"] = side_stream_leg(enc, mel, mask, out, audio_s)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_blocks)
     print(json.dumps(result), flush=True)

@@ -153,3 +153,20 @@ def test_create_without_device_reports_it(aenc):
     W = {k: torch.from_numpy(v) for k, v in synth.make_weights(w).items()}
     with pytest.raises(aenc.AencError, match="no HIP device"):
         aenc.Encoder(w.geom, W)
+
+
+def test_cache_content_keys(aenc):
+    """key_of: deterministic, sensitive to one changed value, to dtype and to shape."""
+    import numpy as np
+    a = np.arange(4800, dtype=np.float32)
+    k = aenc.EmbeddingsCache.key_of(a)
+    assert k == aenc.EmbeddingsCache.key_of(a.copy()) == aenc.EmbeddingsCache.key_of(torch.from_numpy(a))
+    assert 0 <= k < 2 ** 64
+    b = a.copy()
+    b[1234] += 1.0
+    assert aenc.EmbeddingsCache.key_of(b) != k
+    assert aenc.EmbeddingsCache.key_of(a.reshape(48, 100)) != k
+    assert aenc.EmbeddingsCache.key_of(a.view(np.int32)) != k
+    bf = torch.from_numpy(a).to(torch.bfloat16)
+    assert aenc.EmbeddingsCache.key_of(bf) == aenc.EmbeddingsCache.key_of(bf.clone())
+    assert aenc.EmbeddingsCache.key_of(bf) != aenc.EmbeddingsCache.key_of(bf.view(torch.int16))
