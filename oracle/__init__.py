@@ -8,5 +8,6 @@ host runtime; the two meet only through the seeded inputs of ``synth``.
 """
 from .encoder import (  # noqa: F401
     gelu, layer_norm, conv1d_k3, sinusoids, linear, attention, attention_core, block, blocks, stem,
-    final, encode_clip, encode, param_count, param_shapes, flops,
+    final, encode_clip, encode, param_count, param_shapes, flops, chunk_allowed, attended_pairs,
+    CHUNK_CAUSAL, CHUNK_BLOCK,
 )

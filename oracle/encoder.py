@@ -103,9 +103,34 @@ def _f(a, dtype):
     return np.asarray(a, dtype=dtype)
 
 
+CHUNK_CAUSAL = 1
+CHUNK_BLOCK = 2
+
+
+def chunk_allowed(t: int, chunk: int, mode: int) -> np.ndarray:
+    """allowed[q, k] of chunked attention over t positions (parity unpinned as
+    a reading: "MiniCPM-o-2_6", section "(2) AUDIO", prints audio_chunk_length
+    1.0 next to its Whisper encoder but not what the encoder does with it).
+
+    Positions are cut into chunks of `chunk` consecutive positions, c(p) =
+    floor(p / chunk). Chunk-causal (mode 1): query q sees key k when
+    c(k) <= c(q), i.e. its own chunk and every earlier one, as a streaming
+    encoder that is fed one chunk at a time would. Block-diagonal (mode 2):
+    c(k) == c(q). chunk 0 or mode 0: every key is allowed.
+    """
+    if chunk <= 0 or mode == 0:
+        return np.ones((t, t), dtype=bool)
+    c = np.arange(t) // chunk
+    if mode == CHUNK_CAUSAL:
+        return c[None, :] <= c[:, None]
+    if mode == CHUNK_BLOCK:
+        return c[None, :] == c[:, None]
+    raise ValueError(f"chunk mode {mode} must be 0, 1 or 2")
+
+
 def attention(a: np.ndarray, lw: Dict[str, np.ndarray], n_heads: int,
               key_mask: Optional[np.ndarray] = None, k_bias: Optional[np.ndarray] = None,
-              return_probs: bool = False, dtype=np.float64):
+              return_probs: bool = False, dtype=np.float64, allowed: Optional[np.ndarray] = None):
     """Bidirectional multi-head self-attention with an output projection.
 
     One pass over all positions, no causal mask and nothing cached ("Qwen2-
@@ -118,17 +143,19 @@ def attention(a: np.ndarray, lw: Dict[str, np.ndarray], n_heads: int,
     q = linear(a, _f(lw["q_w"], dtype), _f(lw["q_b"], dtype))
     k = linear(a, _f(lw["k_w"], dtype), None if k_bias is None else _f(k_bias, dtype))
     v = linear(a, _f(lw["v_w"], dtype), _f(lw["v_b"], dtype))
-    o, p = attention_core(q, k, v, n_heads, key_mask)
+    o, p = attention_core(q, k, v, n_heads, key_mask, allowed)
     out = linear(o, _f(lw["o_w"], dtype), _f(lw["o_b"], dtype))
     return (out, p) if return_probs else out
 
 
 def attention_core(q: np.ndarray, k: np.ndarray, v: np.ndarray, n_heads: int,
-                   key_mask: Optional[np.ndarray] = None):
+                   key_mask: Optional[np.ndarray] = None, allowed: Optional[np.ndarray] = None):
     """Per head h: softmax_j(Q_h K_h^T / sqrt(dh)) V_h, heads concatenated.
 
-    q, k, v [T, d] -> (o [T, d], probabilities [H, T, T]). Masked keys get
-    probability 0; each row is normalised after subtracting its maximum.
+    q, k, v [T, d] -> (o [T, d], probabilities [H, T, T]). Keys with
+    key_mask == 0, and keys with allowed[q, k] False, get probability 0; each
+    row is normalised after subtracting its maximum. A row left with no key
+    at all (only possible for a masked query under a chunk rule) is zero.
     """
     t, d = q.shape
     dh = d // n_heads
@@ -136,22 +163,31 @@ def attention_core(q: np.ndarray, k: np.ndarray, v: np.ndarray, n_heads: int,
     kh = k.reshape(t, n_heads, dh).transpose(1, 0, 2)
     vh = v.reshape(t, n_heads, dh).transpose(1, 0, 2)
     s = (qh @ kh.transpose(0, 2, 1)) / math.sqrt(dh)          # [H, T, T]
+    ok = np.ones((t, t), dtype=bool)
     if key_mask is not None:
-        s = np.where(np.asarray(key_mask, bool)[None, None, :], s, -np.inf)
-    s = s - s.max(axis=-1, keepdims=True)
-    p = np.exp(s)
-    p = p / p.sum(axis=-1, keepdims=True)
+        ok &= np.asarray(key_mask, bool)[None, :]
+    if allowed is not None:
+        ok &= np.asarray(allowed, bool)
+    if key_mask is not None or allowed is not None:
+        s = np.where(ok[None], s, -np.inf)
+    empty = ~ok.any(axis=1)                                     # [T]
+    m = s.max(axis=-1, keepdims=True)
+    m = np.where(empty[None, :, None], 0.0, m)
+    p = np.exp(s - m)
+    den = p.sum(axis=-1, keepdims=True)
+    p = p / np.where(empty[None, :, None], 1.0, den)
     o = (p @ vh).transpose(1, 0, 2).reshape(t, d)
     return o, p
 
 
 def block(x: np.ndarray, lw: Dict[str, np.ndarray], n_heads: int,
           key_mask: Optional[np.ndarray] = None, eps: float = LN_EPS,
-          k_bias: Optional[np.ndarray] = None, dtype=np.float64) -> np.ndarray:
+          k_bias: Optional[np.ndarray] = None, dtype=np.float64,
+          allowed: Optional[np.ndarray] = None) -> np.ndarray:
     """One pre-LayerNorm block: x + Attn(LN1 x), then + FFN(LN2 x) with
     FFN(h) = GELU(h W1^T + b1) W2^T + b2 (encoder_ffn_dim wide)."""
     a = layer_norm(x, _f(lw["ln1_g"], dtype), _f(lw["ln1_b"], dtype), eps)
-    x = x + attention(a, lw, n_heads, key_mask, k_bias=k_bias, dtype=dtype)
+    x = x + attention(a, lw, n_heads, key_mask, k_bias=k_bias, dtype=dtype, allowed=allowed)
     h = layer_norm(x, _f(lw["ln2_g"], dtype), _f(lw["ln2_b"], dtype), eps)
     h = gelu(linear(h, _f(lw["fc1_w"], dtype), _f(lw["fc1_b"], dtype)))
     return x + linear(h, _f(lw["fc2_w"], dtype), _f(lw["fc2_b"], dtype))
@@ -163,9 +199,10 @@ def layer_weights(W: Dict[str, np.ndarray], layer: int) -> Dict[str, np.ndarray]
 
 
 def blocks(x: np.ndarray, W: Dict[str, np.ndarray], n_layers: int, n_heads: int,
-           key_mask: Optional[np.ndarray] = None, eps: float = LN_EPS, dtype=np.float64) -> np.ndarray:
+           key_mask: Optional[np.ndarray] = None, eps: float = LN_EPS, dtype=np.float64,
+           allowed: Optional[np.ndarray] = None) -> np.ndarray:
     for layer in range(n_layers):
-        x = block(x, layer_weights(W, layer), n_heads, key_mask, eps, dtype=dtype)
+        x = block(x, layer_weights(W, layer), n_heads, key_mask, eps, dtype=dtype, allowed=allowed)
     return x
 
 
@@ -237,7 +274,9 @@ def encode_clip(geom, W: Dict[str, np.ndarray], mel: np.ndarray,
     geometry's depth (used to time a bounded sample)."""
     depth = geom.n_layers if n_layers is None else n_layers
     x = stem(mel, W, dtype)
-    x = blocks(x, W, depth, geom.n_heads, key_mask, geom.ln_eps, dtype)
+    chunk = getattr(geom, "attn_chunk", 0)
+    allowed = chunk_allowed(x.shape[0], chunk, getattr(geom, "attn_chunk_mode", 0)) if chunk else None
+    x = blocks(x, W, depth, geom.n_heads, key_mask, geom.ln_eps, dtype, allowed=allowed)
     return final(x, W, geom.pool_step, geom.ln_eps, dtype, getattr(geom, "stack", 1))
 
 
@@ -281,6 +320,18 @@ def param_count(geom, with_projector: bool = True) -> int:
                if with_projector or not n.startswith("proj"))
 
 
+def attended_pairs(tb: int, chunk: int = 0, mode: int = 0) -> int:
+    """(query, key) pairs among tb valid positions that the chunk rule allows."""
+    if chunk <= 0 or mode == 0:
+        return tb * tb
+    total = 0
+    for q in range(tb):
+        c = q // chunk
+        hi = min(tb, chunk * (c + 1))
+        total += hi - (chunk * c if mode == CHUNK_BLOCK else 0)
+    return total
+
+
 def flops(geom, frames: Optional[Sequence[int]] = None) -> float:
     """Algorithmic FLOPs (2 per multiply-add) of one forward.
 
@@ -295,7 +346,8 @@ def flops(geom, frames: Optional[Sequence[int]] = None) -> float:
         tb = (int(nf) + 1) // 2
         total += 2.0 * nf * d * 3 * m                     # conv1
         total += 2.0 * tb * d * 3 * d                     # conv2
-        per_layer = 2.0 * tb * (3 * d * d + d * d + 2 * d * f) + 4.0 * tb * tb * d
+        pairs = attended_pairs(tb, getattr(geom, "attn_chunk", 0), getattr(geom, "attn_chunk_mode", 0))
+        per_layer = 2.0 * tb * (3 * d * d + d * d + 2 * d * f) + 4.0 * pairs * d
         total += geom.n_layers * per_layer
         if geom.proj_hidden:
             k = getattr(geom, "stack", 1)

@@ -9,6 +9,9 @@ Geometry facts come from the model records on the pages:
     "Preprocessor" (nb_max_frames, hop 160 at 16 kHz = 100 frames/s).
   * Whisper-medium encoder (d_model 1024, 24 layers, 16 heads, FFN 4096) and
     audio_pool_step 2: "MiniCPM-o-2_6", section "(2) AUDIO".
+  * audio_chunk_length 1.0 next to the Whisper-medium encoder: "MiniCPM-o-2_6",
+    section "(2) AUDIO" (the pages print the field without its semantics;
+    the chunked attention workload takes it as 1 s = 50 positions per chunk).
   * 2-layer GELU projector into the 3072-wide LLM: "Voxtral-Mini-3B-2507",
     section "PROJECTOR".
   * Stacking 4 consecutive encoder positions into one 5120-wide projector
@@ -43,6 +46,8 @@ class Geometry:
     out_dtype: str = F32
     ln_eps: float = 1e-5
     stack: int = 1         # positions concatenated into one projector input row (1 or 4)
+    attn_chunk: int = 0    # positions per attention chunk (0: every position sees every position)
+    attn_chunk_mode: int = 0   # with attn_chunk: 1 chunk-causal, 2 block-diagonal
 
     @property
     def n_pos(self) -> int:
@@ -110,6 +115,12 @@ WORKLOADS: Dict[str, Workload] = {
             "whisper_medium_pool2_b1",
             Geometry(batch=1, pool_step=2, **WHISPER_MEDIUM),
             description="Whisper-medium encoder, bf16, batch 1, average pool step 2 -> 750 tokens",
+        ),
+        Workload(
+            "whisper_medium_pool2_chunk1s_b16",
+            Geometry(batch=16, pool_step=2, attn_chunk=50, attn_chunk_mode=1, **WHISPER_MEDIUM),
+            description="Whisper-medium encoder, bf16, batch 16, pool step 2, attention in 1 s chunks "
+                        "(50 positions), each chunk seeing itself and the chunks before it",
         ),
         Workload(
             "whisper_large_b1",

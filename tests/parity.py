@@ -114,6 +114,7 @@ FULL_SIZE_SAMPLES = {
     "whisper_large_proj_b16": dict(clips=[0, 15], every=5),
     "whisper_large_stack4_proj_b16": dict(clips=[0, 15], every=3),
     "whisper_large_varlen_b32": dict(clips=None, every=5),   # shortest, longest and one in between
+    "whisper_medium_pool2_chunk1s_b16": dict(clips=[0, 15], every=3),
 }
 
 
