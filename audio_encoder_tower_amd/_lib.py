@@ -23,7 +23,7 @@ class Geometry(ctypes.Structure):
     _fields_ = [("batch", c_int32), ("n_mel", c_int32), ("n_frames", c_int32), ("d_model", c_int32),
                 ("n_layers", c_int32), ("n_heads", c_int32), ("d_ffn", c_int32), ("pool_step", c_int32),
                 ("proj_hidden", c_int32), ("proj_out", c_int32), ("dtype", c_int32), ("out_dtype", c_int32),
-                ("ln_eps", c_float), ("stack", c_int32)]
+                ("ln_eps", c_float), ("stack", c_int32), ("attn_chunk", c_int32), ("attn_chunk_mode", c_int32)]
 
 
 LAYER_FIELDS = ("ln1_g", "ln1_b", "q_w", "q_b", "k_w", "v_w", "v_b", "o_w", "o_b",
@@ -69,7 +69,9 @@ SIGNATURES = {
                                  c_int, c_int, c_void_p]),
     "aenc_k_qkv_bf16": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_int, c_int, c_void_p]),
     "aenc_k_attention_bf16": (c_int, [c_void_p, c_void_p, c_int64, c_void_p, c_void_p, c_int, c_int, c_int,
-                                      c_void_p, c_void_p]),
+                                      c_void_p, c_void_p, c_void_p, c_void_p]),
+    "aenc_k_chunk_ranges": (c_int, [c_void_p, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p,
+                                    c_void_p]),
     "aenc_k_layernorm": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_float, c_void_p]),
     "aenc_k_gelu_f32": (c_int, [c_void_p, c_void_p, c_int64, c_void_p]),
     "aenc_k_row_maps": (c_int, [c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
@@ -135,4 +137,5 @@ def geometry(g) -> Geometry:
                     n_layers=g.n_layers, n_heads=g.n_heads, d_ffn=g.d_ffn, pool_step=g.pool_step,
                     proj_hidden=g.proj_hidden, proj_out=g.proj_out, dtype=dtype_code(g.dtype),
                     out_dtype=dtype_code(g.out_dtype), ln_eps=g.ln_eps,
-                    stack=getattr(g, "stack", 1))
+                    stack=getattr(g, "stack", 1), attn_chunk=getattr(g, "attn_chunk", 0),
+                    attn_chunk_mode=getattr(g, "attn_chunk_mode", 0))

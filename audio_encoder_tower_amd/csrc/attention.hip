@@ -40,11 +40,18 @@ constexpr int ATT_D = 64;
 // and 16 consecutive rows reading the same chunk use 16 distinct bank groups.
 __device__ __forceinline__ int att_swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
 
+// RANGED: query row r (clip-relative index i) sees only the clip's keys
+// [key_lo[r], key_hi[r]), non-empty and non-decreasing in i (the chunk rules);
+// the workgroup walks the key tiles between its first query's key_lo and its
+// last query's key_hi and masks per query.
+template <bool RANGED>
 __global__ __launch_bounds__(256) void attention_bf16_kernel(const bf16_t* __restrict__ qk, int64_t ld_qk,
                                                              const bf16_t* __restrict__ vt, int64_t ld_vt,
                                                              const int32_t* __restrict__ starts,
                                                              const int32_t* __restrict__ lens, int d,
-                                                             bf16_t* __restrict__ o, int64_t ld_o) {
+                                                             bf16_t* __restrict__ o, int64_t ld_o,
+                                                             const int32_t* __restrict__ key_lo,
+                                                             const int32_t* __restrict__ key_hi) {
   __shared__ __align__(16) bf16_t Ks[2][ATT_BK * ATT_D];   // [key][dim], swizzled 16-byte chunks
   __shared__ __align__(16) bf16_t Vs[2][ATT_D * ATT_BK];   // [dim][key position], swizzled
 
@@ -57,6 +64,14 @@ __global__ __launch_bounds__(256) void attention_bf16_kernel(const bf16_t* __res
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int fq = lane & 31, hh = lane >> 5;
   const int qi = q0 + wave * 32 + fq;                       // this lane's query (clip-relative)
+  // keys this lane's query may see, and the key tiles the workgroup visits
+  int k_lo = 0, k_hi = len, kt_first = 0, kt_last = (len - 1) / ATT_BK;
+  if (RANGED) {
+    k_lo = key_lo[start + min(qi, len - 1)];
+    k_hi = key_hi[start + min(qi, len - 1)];
+    kt_first = key_lo[start + q0] / ATT_BK;
+    kt_last = (key_hi[start + min(q0 + ATT_BQ, len) - 1] - 1) / ATT_BK;
+  }
 
   // Q fragments (B operand of S^T = K Q^T): dims 16s + 8hh .. +7.
   bf16x8 qf[4];
@@ -152,7 +167,16 @@ __global__ __launch_bounds__(256) void attention_bf16_kernel(const bf16_t* __res
       }
     }
     // lane holds keys 32 sub + 8 (v >> 2) + 4 hh + (v & 3) of query qi
-    if (RAGGED) {
+    if (RANGED) {
+      const int first = k0 + 4 * hh;
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int key = first + 32 * sub + 8 * (v >> 2) + (v & 3);
+          if (key < k_lo || key >= k_hi) s[sub][v] = -INFINITY;
+        }
+    } else if (RAGGED) {
       const int nvalid = len - k0 - 4 * hh;
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
@@ -170,7 +194,8 @@ __global__ __launch_bounds__(256) void attention_bf16_kernel(const bf16_t* __res
     // the slack (a uniform branch, rarely taken after the first tile).
     if (__any(mx > m_run + slack)) {
       const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+      // RANGED: a row may still have seen no key at all (both -inf)
+      const float alpha = (RANGED && m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f((m_run - m_new) * c);
       m_run = m_new;
       l_run *= alpha;
 #pragma unroll
@@ -178,7 +203,7 @@ __global__ __launch_bounds__(256) void attention_bf16_kernel(const bf16_t* __res
 #pragma unroll
         for (int v = 0; v < 16; ++v) oacc[es][v] *= alpha;
     }
-    const float mc = m_run * c;
+    const float mc = (RANGED && m_run == -INFINITY) ? 0.0f : m_run * c;
 
     float lsum = 0.0f;
     bf16x8 pb[2][2];
@@ -208,23 +233,38 @@ __global__ __launch_bounds__(256) void attention_bf16_kernel(const bf16_t* __res
     }
   };
 
-  const int n_tiles = (len + ATT_BK - 1) / ATT_BK;
-  if (n_tiles == 1) gload(0, std::true_type{});
-  else gload(0, std::false_type{});
-  lstore(0);
-  __syncthreads();
-  // full tiles: prefetch the next tile into registers while this one computes
-  for (int kt = 0; kt + 1 < n_tiles; ++kt) {
-    const int buf = kt & 1;
-    const int k0 = kt * ATT_BK;
-    if (kt + 2 == n_tiles) gload(k0 + ATT_BK, std::true_type{});
-    else gload(k0 + ATT_BK, std::false_type{});
-    tile(buf, k0, std::false_type{});
-    lstore(buf ^ 1);
+  if (RANGED) {
+    // every tile clamps its key rows and zeroes values past the clip
+    gload(kt_first * ATT_BK, std::true_type{});
+    lstore(0);
     __syncthreads();
+    for (int kt = kt_first; kt < kt_last; ++kt) {
+      const int buf = (kt - kt_first) & 1;
+      gload((kt + 1) * ATT_BK, std::true_type{});
+      tile(buf, kt * ATT_BK, std::true_type{});
+      lstore(buf ^ 1);
+      __syncthreads();
+    }
+    tile((kt_last - kt_first) & 1, kt_last * ATT_BK, std::true_type{});
+  } else {
+    const int n_tiles = kt_last + 1;
+    if (n_tiles == 1) gload(0, std::true_type{});
+    else gload(0, std::false_type{});
+    lstore(0);
+    __syncthreads();
+    // full tiles: prefetch the next tile into registers while this one computes
+    for (int kt = 0; kt + 1 < n_tiles; ++kt) {
+      const int buf = kt & 1;
+      const int k0 = kt * ATT_BK;
+      if (kt + 2 == n_tiles) gload(k0 + ATT_BK, std::true_type{});
+      else gload(k0 + ATT_BK, std::false_type{});
+      tile(buf, k0, std::false_type{});
+      lstore(buf ^ 1);
+      __syncthreads();
+    }
+    // the last tile may be ragged
+    tile((n_tiles - 1) & 1, (n_tiles - 1) * ATT_BK, std::true_type{});
   }
-  // the last tile may be ragged
-  tile((n_tiles - 1) & 1, (n_tiles - 1) * ATT_BK, std::true_type{});
 
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = 1.0f / l_tot;
@@ -245,11 +285,15 @@ __global__ __launch_bounds__(256) void attention_bf16_kernel(const bf16_t* __res
 
 hipError_t attention_bf16(const bf16_t* qk, int64_t ld_qk, const bf16_t* vt, int64_t ld_vt, const int32_t* start,
                           const int32_t* len, int n_clips, int max_len, int n_heads, bf16_t* o, int64_t ld_o,
-                          hipStream_t stream) {
-  if (n_clips <= 0 || max_len <= 0 || n_heads <= 0) return hipErrorInvalidValue;
+                          const int32_t* key_lo, const int32_t* key_hi, hipStream_t stream) {
+  if (n_clips <= 0 || max_len <= 0 || n_heads <= 0 || (!key_lo != !key_hi)) return hipErrorInvalidValue;
   dim3 grid((max_len + ATT_BQ - 1) / ATT_BQ, n_heads, n_clips);
-  hipLaunchKernelGGL(attention_bf16_kernel, grid, dim3(256), 0, stream, qk, ld_qk, vt, ld_vt, start, len,
-                     n_heads * ATT_D, o, ld_o);
+  if (key_lo)
+    hipLaunchKernelGGL(attention_bf16_kernel<true>, grid, dim3(256), 0, stream, qk, ld_qk, vt, ld_vt, start, len,
+                       n_heads * ATT_D, o, ld_o, key_lo, key_hi);
+  else
+    hipLaunchKernelGGL(attention_bf16_kernel<false>, grid, dim3(256), 0, stream, qk, ld_qk, vt, ld_vt, start, len,
+                       n_heads * ATT_D, o, ld_o, nullptr, nullptr);
   return hipGetLastError();
 }
 
@@ -260,7 +304,9 @@ hipError_t attention_bf16(const bf16_t* qk, int64_t ld_qk, const bf16_t* vt, int
 __global__ __launch_bounds__(64) void attention_f32_kernel(const float* __restrict__ qkv, int64_t ld,
                                                            const int32_t* __restrict__ starts,
                                                            const int32_t* __restrict__ lens, int d,
-                                                           float* __restrict__ o, int64_t ld_o) {
+                                                           float* __restrict__ o, int64_t ld_o,
+                                                           const int32_t* __restrict__ key_lo,
+                                                           const int32_t* __restrict__ key_hi) {
   __shared__ float Ks[ATT_BK][ATT_D + 1];
   __shared__ float Vs[ATT_BK][ATT_D + 1];
   const int b = blockIdx.z, h = blockIdx.y;
@@ -274,6 +320,9 @@ __global__ __launch_bounds__(64) void attention_f32_kernel(const float* __restri
   const float* qrow = qkv + (int64_t)(start + qi) * ld + h * ATT_D;
 #pragma unroll
   for (int e = 0; e < ATT_D; ++e) { q[e] = qrow[e] * 0.125f; acc[e] = 0.0f; }
+  // keys [lo, hi) of this query (all of the clip without ranges)
+  const int lo = key_lo ? key_lo[start + qi] : 0;
+  const int hi = key_hi ? key_hi[start + qi] : len;
   float m_run = -INFINITY, l_run = 0.0f;
   for (int k0 = 0; k0 < len; k0 += ATT_BK) {
     __syncthreads();
@@ -291,10 +340,11 @@ __global__ __launch_bounds__(64) void attention_f32_kernel(const float* __restri
       float v = 0.0f;
 #pragma unroll
       for (int e = 0; e < ATT_D; ++e) v = fmaf(q[e], Ks[j][e], v);
-      s[j] = j < nk ? v : -INFINITY;
+      s[j] = (j < nk && k0 + j >= lo && k0 + j < hi) ? v : -INFINITY;
       mx = fmaxf(mx, s[j]);
     }
     const float m_new = fmaxf(m_run, mx);
+    if (m_new == -INFINITY) continue;   // no key of this query in the tile yet
     const float alpha = expf(m_run - m_new);
     l_run *= alpha;
 #pragma unroll
@@ -316,11 +366,12 @@ __global__ __launch_bounds__(64) void attention_f32_kernel(const float* __restri
 }
 
 hipError_t attention_f32(const float* qkv, int64_t ld, const int32_t* start, const int32_t* len, int n_clips,
-                         int max_len, int n_heads, float* o, int64_t ld_o, hipStream_t stream) {
-  if (n_clips <= 0 || max_len <= 0 || n_heads <= 0) return hipErrorInvalidValue;
+                         int max_len, int n_heads, float* o, int64_t ld_o, const int32_t* key_lo,
+                         const int32_t* key_hi, hipStream_t stream) {
+  if (n_clips <= 0 || max_len <= 0 || n_heads <= 0 || (!key_lo != !key_hi)) return hipErrorInvalidValue;
   dim3 grid((max_len + 63) / 64, n_heads, n_clips);
   hipLaunchKernelGGL(attention_f32_kernel, grid, dim3(64), 0, stream, qkv, ld, start, len, n_heads * ATT_D, o,
-                     ld_o);
+                     ld_o, key_lo, key_hi);
   return hipGetLastError();
 }
 

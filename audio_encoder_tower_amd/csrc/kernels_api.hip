@@ -66,13 +66,24 @@ extern "C" int aenc_k_qkv_bf16(const void* A, const void* Wqkv, const float* bia
 }
 
 extern "C" int aenc_k_attention_bf16(const void* qk, const void* vt, int64_t ld_vt, const int32_t* start,
-                                     const int32_t* len, int n_clips, int max_len, int n_heads, void* out,
-                                     void* stream) {
+                                     const int32_t* len, int n_clips, int max_len, int n_heads,
+                                     const int32_t* key_lo, const int32_t* key_hi, void* out, void* stream) {
   if (!qk || !vt || !start || !len || !out) return fail("NULL operand");
+  if (!key_lo != !key_hi) return fail("key_lo and key_hi go together");
   if (n_clips < 1 || max_len < 1 || n_heads < 1 || ld_vt % 8) return fail("bad attention sizes");
   const int d = 64 * n_heads;
   return hip_status(attention_bf16((const bf16_t*)qk, 2 * d, (const bf16_t*)vt, ld_vt, start, len, n_clips, max_len,
-                                   n_heads, (bf16_t*)out, d, (hipStream_t)stream), "attention");
+                                   n_heads, (bf16_t*)out, d, key_lo, key_hi, (hipStream_t)stream), "attention");
+}
+
+extern "C" int aenc_k_chunk_ranges(const uint8_t* mask, int B, int T, int chunk, int mode, const int32_t* row_map,
+                                   const int32_t* cu, int32_t* key_lo, int32_t* key_hi, void* stream) {
+  if (!row_map || !cu || !key_lo || !key_hi) return fail("NULL operand");
+  if (B < 1 || T < 1 || T > CHUNK_MAX_T) return fail("B must be >= 1 and T in 1..4096");
+  if (chunk < 1 || (mode != AENC_CHUNK_CAUSAL && mode != AENC_CHUNK_BLOCK))
+    return fail("chunk must be >= 1 and mode AENC_CHUNK_CAUSAL or AENC_CHUNK_BLOCK");
+  return hip_status(build_chunk_ranges(mask, B, T, chunk, mode, row_map, cu, key_lo, key_hi, (hipStream_t)stream),
+                    "chunk ranges");
 }
 
 extern "C" int aenc_k_layernorm(const float* x, const float* gamma, const float* beta, void* y, int y_dtype, int M,

@@ -23,13 +23,17 @@ hipError_t gemm_f32(int epi, const float* A, RowMap arow, const float* W, int64_
 // column h*64 and K at column d + h*64; vt: V transposed, row (h*64 + e) holds
 // feature e of head h for every packed row, ld_vt apart. Clip b owns packed rows
 // [start[b], start[b] + len[b]); start[b] % 8 == 0. o: [rows, ld_o] bf16, head h at column h*64.
+// key_lo/key_hi (both or neither): per packed row, the clip-relative keys
+// [key_lo, key_hi) it sees, non-empty and non-decreasing along the clip.
 hipError_t attention_bf16(const bf16_t* qk, int64_t ld_qk, const bf16_t* vt, int64_t ld_vt,
                           const int32_t* start, const int32_t* len, int n_clips, int max_len, int n_heads,
-                          bf16_t* o, int64_t ld_o, hipStream_t stream);
+                          bf16_t* o, int64_t ld_o, const int32_t* key_lo, const int32_t* key_hi,
+                          hipStream_t stream);
 
 // The same for the fp32 path with row-major V: qkv [rows, 3d] (Q | K | V).
 hipError_t attention_f32(const float* qkv, int64_t ld, const int32_t* start, const int32_t* len, int n_clips,
-                         int max_len, int n_heads, float* o, int64_t ld_o, hipStream_t stream);
+                         int max_len, int n_heads, float* o, int64_t ld_o, const int32_t* key_lo,
+                         const int32_t* key_hi, hipStream_t stream);
 
 // LayerNorm of fp32 rows: y[r] = LN(x[r]) for r < M (M = *m_dev if set).
 hipError_t layernorm(const float* x, const float* gamma, const float* beta, void* y, int y_dtype, int M,
@@ -63,6 +67,13 @@ hipError_t build_row_maps(const uint8_t* mask, int B, int T, int32_t* row_map, i
 // are all valid (k j + k <= lens[b]), else -1. inv_map [B * round_up(T, 8) / k]:
 // the inverse, -1 for stacked rows that are no output row. m_valid [1]:
 // stacked rows to compute, ceil(cu[B] / k). k divides 8.
+// Chunked attention: per packed row, the clip-relative key range [key_lo, key_hi)
+// of the chunk rule (mode 1 chunk-causal, 2 block-diagonal, `chunk` positions
+// per chunk) from the key mask (NULL = all valid) and the packing maps of
+// build_row_maps. T <= CHUNK_MAX_T.
+constexpr int CHUNK_MAX_T = 4096;
+hipError_t build_chunk_ranges(const uint8_t* mask, int B, int T, int chunk, int mode, const int32_t* row_map,
+                              const int32_t* cu, int32_t* key_lo, int32_t* key_hi, hipStream_t stream);
 hipError_t build_stack_maps(const int32_t* cu, const int32_t* lens, int B, int T, int k, int32_t* row_map,
                             int32_t* inv_map, int32_t* m_valid, hipStream_t stream);
 

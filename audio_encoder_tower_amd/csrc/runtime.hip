@@ -92,6 +92,8 @@ struct aenc_handle {
   // stacked projector rows (stack > 1): output row -> stacked row, stacked row -> output row, row count
   int32_t *sk_row_map = nullptr, *sk_inv_map = nullptr, *sk_m_valid = nullptr;
   int32_t *id_sk_row_map = nullptr, *id_sk_inv_map = nullptr, *id_sk_m_valid = nullptr;
+  // chunked attention: per packed row, the clip-relative keys [key_lo, key_hi) it sees
+  int32_t *key_lo = nullptr, *key_hi = nullptr, *id_key_lo = nullptr, *id_key_hi = nullptr;
 
   // profiling
   bool prof = false;
@@ -158,6 +160,16 @@ extern "C" int aenc_validate(const aenc_geometry* g) {
     set_error("stack 4 needs at least 4 positions (n_frames >= 8)");
     return AENC_E_INVAL;
   }
+  if (g->attn_chunk < 0 || g->attn_chunk > g->n_frames / 2) {
+    set_error("attn_chunk %d outside 0..n_frames/2", g->attn_chunk);
+    return AENC_E_INVAL;
+  }
+  if (g->attn_chunk == 0 ? g->attn_chunk_mode != AENC_CHUNK_NONE
+                         : (g->attn_chunk_mode != AENC_CHUNK_CAUSAL && g->attn_chunk_mode != AENC_CHUNK_BLOCK)) {
+    set_error("attn_chunk_mode %d: AENC_CHUNK_CAUSAL or AENC_CHUNK_BLOCK with attn_chunk > 0, else AENC_CHUNK_NONE",
+              g->attn_chunk_mode);
+    return AENC_E_INVAL;
+  }
   return AENC_OK;
 }
 
@@ -221,7 +233,9 @@ Layout workspace_layout(const aenc_geometry* g) {
   const int k = stack_of(g);
   const size_t maps = (size_t)(B * L.T + L.M_cap + (B + 1) + B + 1) * 4;
   const size_t sk_maps = k > 1 ? (size_t)(B * (L.T / k) + L.M_cap / k + 1) * 4 : 0;
-  L.off_maps = take(2 * maps + 2 * sk_maps + 64);
+  // chunked attention: key_lo and key_hi per packed row, twice
+  const size_t ranges = g->attn_chunk > 0 ? (size_t)2 * L.M_cap * 4 : 0;
+  L.off_maps = take(2 * maps + 2 * sk_maps + 2 * ranges + 64);
   L.total = off;
   return L;
 }
@@ -413,6 +427,14 @@ bool build(aenc_handle* h, const aenc_weights* w) {
     HIP_TRY(build_stack_maps(h->id_cu, h->id_lens, g.batch, h->T, k, h->id_sk_row_map, h->id_sk_inv_map,
                              h->id_sk_m_valid, nullptr));
   }
+  if (g.attn_chunk > 0) {
+    h->key_lo = maps; maps += h->M_cap;
+    h->key_hi = maps; maps += h->M_cap;
+    h->id_key_lo = maps; maps += h->M_cap;
+    h->id_key_hi = maps; maps += h->M_cap;
+    HIP_TRY(build_chunk_ranges(nullptr, g.batch, h->T, g.attn_chunk, g.attn_chunk_mode, h->id_row_map, h->id_cu,
+                               h->id_key_lo, h->id_key_hi, nullptr));
+  }
   HIP_TRY(hipDeviceSynchronize());
   return true;
 }
@@ -453,7 +475,7 @@ extern "C" aenc_handle* aenc_create(const aenc_geometry* g, const aenc_weights* 
   h->device = dev;
   const Layout Ly = workspace_layout(g);
   h->T = Ly.T; h->T8 = Ly.T8; h->C_pad = Ly.C_pad; h->M_cap = Ly.M_cap; h->ld_vt = Ly.ld_vt; h->esz = Ly.esz;
-  h->launches_per_forward = 7 * g->n_layers + 9;
+  h->launches_per_forward = 7 * g->n_layers + 10;
   if (!build(h, w)) {
     std::string msg = g_last_error;
     release(h);
@@ -591,6 +613,14 @@ extern "C" int aenc_forward(aenc_handle* h, const void* mel, const uint8_t* mask
       sk_row_map = h->sk_row_map; sk_inv_map = h->sk_inv_map; sk_mv = h->sk_m_valid;
     }
   }
+  const int32_t *key_lo = h->id_key_lo, *key_hi = h->id_key_hi;
+  if (mask && g.attn_chunk > 0) {
+    if (!q.done(K_MAPS, build_chunk_ranges(mask, B, T, g.attn_chunk, g.attn_chunk_mode, row_map, cu, h->key_lo,
+                                           h->key_hi, s),
+                "chunk ranges"))
+      return AENC_E_HIP;
+    key_lo = h->key_lo; key_hi = h->key_hi;
+  }
   // Rows of the packed layout the GEMMs must cover at most (all clips full).
   const int M_rows = (int)((int64_t)(B - 1) * h->T8 + T);
 
@@ -652,9 +682,9 @@ extern "C" int aenc_forward(aenc_handle* h, const void* mel, const uint8_t* mask
 
     if (bf)
       e = attention_bf16((const bf16_t*)h->qk, 2 * d, (const bf16_t*)h->vt, h->ld_vt, cu, lens, B, T, g.n_heads,
-                         (bf16_t*)h->a, d, s);
+                         (bf16_t*)h->a, d, key_lo, key_hi, s);
     else
-      e = attention_f32((const float*)h->qk, 3 * d, cu, lens, B, T, g.n_heads, (float*)h->a, d, s);
+      e = attention_f32((const float*)h->qk, 3 * d, cu, lens, B, T, g.n_heads, (float*)h->a, d, key_lo, key_hi, s);
     if (!q.done(K_ATTN, e, "attention")) return AENC_E_HIP;
 
     EpiParams eo{};

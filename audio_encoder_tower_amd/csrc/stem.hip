@@ -128,6 +128,64 @@ hipError_t build_row_maps(const uint8_t* mask, int B, int T, int32_t* row_map, i
   return hipGetLastError();
 }
 
+// Key ranges of chunked attention. Positions t of a clip fall into chunks of
+// `chunk` consecutive positions, c(t) = t / chunk; a query sees the keys of its
+// own chunk and, chunk-causal (mode 1), every earlier chunk, or, block-diagonal
+// (mode 2), only its own. Packing keeps the clip's valid positions in order, so
+// those keys are one contiguous range of the clip's packed rows: with cnt[p]
+// the number of valid positions before position p, query t sees packed keys
+// [mode 2 ? cnt[chunk c] : 0, cnt[min(T, chunk (c + 1))]). One workgroup per
+// clip: cnt by a block scan of the mask in LDS, then one range per valid row.
+__global__ __launch_bounds__(SCAN_THREADS) void chunk_ranges_kernel(const uint8_t* __restrict__ mask, int T,
+                                                                    int chunk, int mode,
+                                                                    const int32_t* __restrict__ row_map,
+                                                                    const int32_t* __restrict__ cu,
+                                                                    int32_t* __restrict__ key_lo,
+                                                                    int32_t* __restrict__ key_hi) {
+  __shared__ int cnt[CHUNK_MAX_T + 1];
+  __shared__ int wsum[SCAN_THREADS / 64];
+  __shared__ int carry;
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid == 0) carry = 0;
+  __syncthreads();
+  for (int t0 = 0; t0 < T; t0 += SCAN_THREADS) {
+    const int t = t0 + tid;
+    const int valid = (t < T) ? (mask ? (mask[(int64_t)b * T + t] != 0) : 1) : 0;
+    int x = valid;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(x, off, 64);
+      if (lane >= off) x += y;
+    }
+    if (lane == 63) wsum[wave] = x;
+    __syncthreads();
+    int before = carry;
+    for (int w = 0; w < wave; ++w) before += wsum[w];
+    if (t < T) cnt[t] = before + x - valid;      // exclusive count
+    __syncthreads();
+    if (tid == SCAN_THREADS - 1) carry = before + x;
+    __syncthreads();
+  }
+  if (tid == 0) cnt[T] = carry;
+  __syncthreads();
+  const int base = cu[b];
+  for (int t = tid; t < T; t += SCAN_THREADS) {
+    if (row_map[(int64_t)b * T + t] < 0) continue;
+    const int c = t / chunk;
+    const int r = base + cnt[t];
+    key_lo[r] = mode == 2 ? cnt[min(T, chunk * c)] : 0;
+    key_hi[r] = cnt[min(T, chunk * (c + 1))];
+  }
+}
+
+hipError_t build_chunk_ranges(const uint8_t* mask, int B, int T, int chunk, int mode, const int32_t* row_map,
+                              const int32_t* cu, int32_t* key_lo, int32_t* key_hi, hipStream_t stream) {
+  if (B < 1 || T < 1 || T > CHUNK_MAX_T || chunk < 1 || (mode != 1 && mode != 2)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(chunk_ranges_kernel, dim3(B), dim3(SCAN_THREADS), 0, stream, mask, T, chunk, mode, row_map,
+                     cu, key_lo, key_hi);
+  return hipGetLastError();
+}
+
 // One workgroup: clip by clip, every stacked row of the clip's packed range
 // gets its output row (or -1), and every output row its stacked row (or -1).
 __global__ __launch_bounds__(SCAN_THREADS) void stack_maps_kernel(const int32_t* __restrict__ cu,

@@ -50,13 +50,30 @@ def qkv_bf16(a: torch.Tensor, wqkv: torch.Tensor, bias: Optional[torch.Tensor], 
 
 
 def attention_bf16(qk: torch.Tensor, vt: torch.Tensor, start: torch.Tensor, lens: torch.Tensor, max_len: int,
-                   n_heads: int, out: torch.Tensor) -> torch.Tensor:
+                   n_heads: int, out: torch.Tensor, key_lo: Optional[torch.Tensor] = None,
+                   key_hi: Optional[torch.Tensor] = None) -> torch.Tensor:
     d = 64 * n_heads
     assert qk.shape[1] == 2 * d and vt.shape[0] == d and out.shape == (qk.shape[0], d)
     assert start.dtype == lens.dtype == torch.int32 and start.numel() >= lens.numel()
+    assert (key_lo is None) == (key_hi is None)
+    if key_lo is not None:
+        assert key_lo.dtype == key_hi.dtype == torch.int32
+        assert key_lo.numel() >= qk.shape[0] and key_hi.numel() >= qk.shape[0]
     check(lib().aenc_k_attention_bf16(_p(qk), _p(vt), vt.shape[1], _p(start), _p(lens), lens.numel(), max_len,
-                                      n_heads, _p(out), _s()), "aenc_k_attention_bf16")
+                                      n_heads, _p(key_lo), _p(key_hi), _p(out), _s()), "aenc_k_attention_bf16")
     return out
+
+
+CHUNK_MODE = {"causal": 1, "block": 2}
+
+
+def chunk_ranges(mask: Optional[torch.Tensor], B: int, T: int, chunk: int, mode: str, row_map: torch.Tensor,
+                 cu: torch.Tensor, key_lo: torch.Tensor, key_hi: torch.Tensor) -> None:
+    """Per packed row, the clip-relative key range of a chunk rule (aenc_k_chunk_ranges)."""
+    assert mask is None or (mask.dtype == torch.uint8 and mask.shape == (B, T))
+    assert row_map.numel() >= B * T and cu.numel() >= B + 1
+    check(lib().aenc_k_chunk_ranges(_p(mask), B, T, chunk, CHUNK_MODE[mode], _p(row_map), _p(cu), _p(key_lo),
+                                    _p(key_hi), _s()), "aenc_k_chunk_ranges")
 
 
 def layernorm(x: torch.Tensor, gamma: torch.Tensor, beta: torch.Tensor, y: torch.Tensor, eps: float) -> torch.Tensor:

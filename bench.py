@@ -48,7 +48,9 @@ def step_flops(g, kind: str, rows: int, proj_rows: int) -> float:
 
 
 def attention_flops(g, tb) -> float:
-    return float(sum(4.0 * t * t * g.d_model for t in tb))
+    """QK^T and PV over the (query, key) pairs the attention rule allows."""
+    import oracle  # closed-form pair count only
+    return float(sum(4.0 * oracle.attended_pairs(int(t), g.attn_chunk, g.attn_chunk_mode) * g.d_model for t in tb))
 
 
 def cpu_baseline(w, blocks: int = 0):
@@ -355,6 +357,7 @@ def main():
         "config": {"workload": w.name, "global_batch": g.batch, "seq_len": g.n_pos, "mel_frames": g.n_frames,
                    "d_model": g.d_model, "layers": g.n_layers, "heads": g.n_heads, "ffn": g.d_ffn,
                    "pool_step": g.pool_step, "stack": g.stack,
+                   "attn_chunk": [g.attn_chunk, {0: "none", 1: "causal", 2: "block"}[g.attn_chunk_mode]],
                    "projector": [g.proj_in, g.proj_hidden, g.proj_out] if g.proj_hidden else None,
                    "audio_seconds_per_step": audio_s, "parallelism": "none (1 GPU)"},
         "tflops": round(tflops, 1),

@@ -49,6 +49,13 @@ extern "C" {
 /* Element types. */
 enum { AENC_F32 = 0, AENC_BF16 = 1 };
 
+/* Chunked attention rules (aenc_geometry.attn_chunk_mode). */
+enum {
+  AENC_CHUNK_NONE = 0,    /* every position sees every valid position of its clip */
+  AENC_CHUNK_CAUSAL = 1,  /* its own chunk and every earlier chunk                */
+  AENC_CHUNK_BLOCK = 2    /* its own chunk only                                   */
+};
+
 /* Status codes returned by the int-valued functions. */
 typedef enum {
   AENC_OK = 0,
@@ -83,6 +90,14 @@ typedef struct aenc_geometry {
                          * "[WIP][TSS][Model] Kimi-Audio-7B", Purpose; kimia_adaptor_input_dim
                          * 5120, "Kimi-Audio-7B-Instruct", (1) AUDIO). Needs a projector and
                          * pool_step 1.                                                    */
+  int32_t attn_chunk;   /* 0: full bidirectional attention. > 0: positions are cut into
+                         * chunks of attn_chunk consecutive positions (by their position in
+                         * the clip, masked ones included) and attention follows
+                         * attn_chunk_mode. A reading of audio_chunk_length 1.0 printed beside
+                         * MiniCPM-o's Whisper encoder ("MiniCPM-o-2_6", (2) AUDIO): 1 s of
+                         * audio is 50 positions. 0 .. n_frames/2.                          */
+  int32_t attn_chunk_mode; /* AENC_CHUNK_CAUSAL or AENC_CHUNK_BLOCK when attn_chunk > 0,
+                            * AENC_CHUNK_NONE (0) otherwise.                               */
 } aenc_geometry;
 
 /* One block's tensors (d = d_model, f = d_ffn). Pointers may be host or device

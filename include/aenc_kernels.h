@@ -10,8 +10,9 @@
  * come from the same passages: linear maps with [out, in] weights and the
  * gelu activation ("Qwen2-Audio-7B-Instruct", (1) AUDIO ENCODER; "Voxtral-
  * Mini-3B-2507", PROJECTOR), bidirectional multi-head attention with head_dim
- * 64 ("Voxtral-Mini-3B-2507", (1) AUDIO ENCODER) and the LayerNorms of the
- * pre-LN blocks.
+ * 64 ("Voxtral-Mini-3B-2507", (1) AUDIO ENCODER), its chunked variant (a
+ * reading of audio_chunk_length, "MiniCPM-o-2_6", (2) AUDIO) and the
+ * LayerNorms of the pre-LN blocks.
  */
 #ifndef AENC_KERNELS_H
 #define AENC_KERNELS_H
@@ -53,9 +54,24 @@ int aenc_k_qkv_bf16(const void *A, const void *Wqkv, const float *bias, void *qk
  * d + 64h) and the same columns of vt; every start[b] must be a multiple of 8,
  * every len[b] >= 1 and max_len >= the longest clip; vt must hold 64 columns
  * past the end of the last clip. out: bf16 [rows, d], head h at column 64h;
- * rows outside every clip are not written. */
+ * rows outside every clip are not written.
+ * key_lo, key_hi: NULL (every query sees its whole clip) or int32 [rows]: the
+ * query at packed row r sees the clip-relative keys [key_lo[r], key_hi[r]);
+ * within a clip the ranges must be non-empty, inside [0, len[b]] and
+ * non-decreasing in r (as aenc_k_chunk_ranges writes them); not checked. */
 int aenc_k_attention_bf16(const void *qk, const void *vt, int64_t ld_vt, const int32_t *start, const int32_t *len,
-                          int n_clips, int max_len, int n_heads, void *out, void *stream);
+                          int n_clips, int max_len, int n_heads, const int32_t *key_lo, const int32_t *key_hi,
+                          void *out, void *stream);
+
+/* Key ranges of chunked attention (aenc.h, AENC_CHUNK_*): positions of a clip
+ * are cut into chunks of `chunk` consecutive positions; a valid position sees
+ * the valid positions of its own chunk and (mode AENC_CHUNK_CAUSAL) of every
+ * earlier chunk, or (AENC_CHUNK_BLOCK) of its own chunk only. From the key
+ * mask (uint8 [B, T], NULL = all valid) and the packing maps row_map and cu of
+ * aenc_k_row_maps, writes key_lo and key_hi (int32, indexed by packed row,
+ * clip-relative) for every valid position's packed row. T <= 4096. */
+int aenc_k_chunk_ranges(const uint8_t *mask, int B, int T, int chunk, int mode, const int32_t *row_map,
+                        const int32_t *cu, int32_t *key_lo, int32_t *key_hi, void *stream);
 
 /* y[r] = LayerNorm(x[r]; gamma, beta, eps) for r < M, x fp32 [M, d], y in
  * y_dtype (0 fp32, 1 bf16); gamma, beta fp32 [d]. d % 4 == 0, d <= 2048. */

@@ -170,3 +170,30 @@ def test_cache_content_keys(aenc):
     bf = torch.from_numpy(a).to(torch.bfloat16)
     assert aenc.EmbeddingsCache.key_of(bf) == aenc.EmbeddingsCache.key_of(bf.clone())
     assert aenc.EmbeddingsCache.key_of(bf) != aenc.EmbeddingsCache.key_of(bf.view(torch.int16))
+
+
+def test_chunked_attention_geometry(aenc):
+    g = synth.get_workload("whisper_medium_pool2_chunk1s_b16").geom
+    assert aenc.validate(g) == 0
+    assert aenc.output_shape(g) == (16, 750, 1024)
+    # the chunk rule changes no parameter and no shape
+    assert aenc.param_count(g) == aenc.param_count(g.replace(attn_chunk=0, attn_chunk_mode=0))
+    for bad in (dict(attn_chunk=-1), dict(attn_chunk=1501), dict(attn_chunk=50, attn_chunk_mode=0),
+                dict(attn_chunk=50, attn_chunk_mode=3), dict(attn_chunk=0, attn_chunk_mode=1)):
+        assert aenc.validate(g.replace(**bad)) == -1, bad
+        assert "attn_chunk" in aenc.last_error()
+    assert aenc.validate(g.replace(attn_chunk=1500, attn_chunk_mode=2)) == 0
+    # the workspace holds two more int32 per packed row and copy
+    assert aenc.lib().aenc_workspace_bytes(ctypes.byref(aenc._lib.geometry(g))) > \
+        aenc.lib().aenc_workspace_bytes(ctypes.byref(aenc._lib.geometry(g.replace(attn_chunk=0, attn_chunk_mode=0))))
+
+
+def test_chunk_step_rejects_bad_arguments(aenc):
+    L = aenc.lib()
+    p = ctypes.c_void_p(16)      # never dereferenced: every call fails its host checks
+    assert L.aenc_k_chunk_ranges(None, 1, 10, 5, 1, None, p, p, p, None) == -1
+    assert L.aenc_k_chunk_ranges(None, 1, 10, 0, 1, p, p, p, p, None) == -1
+    assert L.aenc_k_chunk_ranges(None, 1, 10, 5, 3, p, p, p, p, None) == -1
+    assert L.aenc_k_chunk_ranges(None, 1, 5000, 5, 1, p, p, p, p, None) == -1
+    assert L.aenc_k_attention_bf16(p, p, 64, p, p, 1, 10, 1, p, None, p, None) == -1
+    assert "together" in aenc.last_error()

@@ -211,3 +211,98 @@ def test_attention_bf16(_lib, lens, heads, scale):
         assert err.max() <= 1e-2 * max(1.0, np.abs(v).max()), (n, err.max())
         cos = (got[sl] * ref).sum(1) / (np.linalg.norm(got[sl], axis=1) * np.linalg.norm(ref, axis=1))
         assert cos.min() >= 0.9999, (n, cos.min())
+
+
+def ranges_from_rule(mask, chunk, mode):
+    """Expected key ranges: for each valid position, the packed rows of the
+    valid keys that oracle.chunk_allowed lets it see, which must be one
+    contiguous run; returned clip-relative, keyed by the query's packed row."""
+    B, T = mask.shape
+    row_map, cu, _ = packing_contract(mask)
+    allowed = oracle.chunk_allowed(T, chunk, mode)
+    lo, hi = {}, {}
+    for b in range(B):
+        valid = mask[b].astype(bool)
+        for t in np.flatnonzero(valid):
+            keys = np.flatnonzero(allowed[t] & valid)
+            packed = row_map[b * T + keys] - cu[b]
+            assert np.array_equal(packed, np.arange(packed[0], packed[-1] + 1)), "rule not contiguous"
+            r = row_map[b * T + t]
+            lo[r], hi[r] = packed[0], packed[-1] + 1
+    return lo, hi
+
+
+@pytest.mark.parametrize("mode", ["causal", "block"])
+@pytest.mark.parametrize("case,chunk", [("prefix", 50), ("random", 50), ("random", 7), ("all_valid", 1),
+                                        ("prefix", 1500), ("single", 1)])
+def test_chunk_ranges(_lib, case, chunk, mode):
+    rng = np.random.default_rng(11)
+    B, T = 4, 1500
+    if case == "all_valid":
+        mask = np.ones((B, T), np.uint8)
+    elif case == "prefix":
+        lens = [1500, 1, 731, 64]
+        mask = (np.arange(T)[None, :] < np.array(lens)[:, None]).astype(np.uint8)
+    elif case == "random":
+        mask = (rng.random((B, T)) > 0.4).astype(np.uint8)
+        mask[:, 0] = 1
+    else:
+        B, T = 1, 1
+        mask = np.ones((1, 1), np.uint8)
+    md = torch.from_numpy(mask).to(DEV)
+    rm, inv, cu, lens, mv = _lib.steps.row_maps(md, B, T)
+    rows = int(B * ((T + 7) // 8 * 8))
+    key_lo = torch.full((rows,), -7, dtype=torch.int32, device=DEV)
+    key_hi = torch.full((rows,), -7, dtype=torch.int32, device=DEV)
+    _lib.steps.chunk_ranges(md, B, T, chunk, mode, rm, cu, key_lo, key_hi)
+    torch.cuda.synchronize()
+    lo, hi = ranges_from_rule(mask, chunk, oracle.CHUNK_CAUSAL if mode == "causal" else oracle.CHUNK_BLOCK)
+    got_lo, got_hi = key_lo.cpu().numpy(), key_hi.cpu().numpy()
+    for r in lo:
+        assert (got_lo[r], got_hi[r]) == (lo[r], hi[r]), (r, got_lo[r], got_hi[r], lo[r], hi[r])
+    untouched = np.setdiff1d(np.arange(rows), np.array(list(lo)))
+    assert np.all(got_lo[untouched] == -7) and np.all(got_hi[untouched] == -7)
+
+
+@pytest.mark.parametrize("lens,heads,chunk,mode", [
+    ([1500], 4, 50, "causal"),
+    ([731, 64, 1, 129], 2, 50, "block"),
+    ([300], 2, 1, "block"),
+    ([300], 2, 1, "causal"),
+    ([257, 511], 3, 128, "causal"),
+    ([1000], 2, 37, "block"),
+    ([200], 2, 500, "causal"),
+], ids=["whisper_large_1s_causal", "ragged_block", "one_block", "one_causal", "tile_aligned", "odd_block",
+        "chunk_covers_clip"])
+def test_attention_bf16_chunked(_lib, lens, heads, chunk, mode):
+    """Ranged attention (ranges from aenc_k_chunk_ranges over all-valid clips)
+    against the oracle's chunked attention on every row."""
+    rng = np.random.default_rng(sum(lens) + chunk)
+    d = 64 * heads
+    B, T = len(lens), max(lens)
+    mask = (np.arange(T)[None, :] < np.array(lens)[:, None]).astype(np.uint8)
+    md = torch.from_numpy(mask).to(DEV)
+    rm, inv, cu_d, ln_d, mv = _lib.steps.row_maps(md, B, T)
+    cu = cu_d.cpu().numpy()
+    rows = int(cu[-1])
+    key_lo = torch.zeros(rows + 8, dtype=torch.int32, device=DEV)
+    key_hi = torch.zeros(rows + 8, dtype=torch.int32, device=DEV)
+    _lib.steps.chunk_ranges(md, B, T, chunk, mode, rm, cu_d, key_lo, key_hi)
+    q, k, v = (bf16(rng, rows, d, scale=1.5) for _ in range(3))
+    ld_vt = (rows + 63) // 64 * 64 + 64
+    qk = np.concatenate([q, k], axis=1)
+    vt = np.zeros((d, ld_vt), np.float32)
+    vt[:, :rows] = v.T
+    out = torch.full((rows, d), float("nan"), device=DEV, dtype=torch.bfloat16)
+    _lib.steps.attention_bf16(dev_bf16(qk), dev_bf16(vt), cu_d, ln_d, T, heads, out, key_lo, key_hi)
+    torch.cuda.synchronize()
+    got = host(out)
+    rule = oracle.CHUNK_CAUSAL if mode == "causal" else oracle.CHUNK_BLOCK
+    for b, n in enumerate(lens):
+        sl = slice(int(cu[b]), int(cu[b]) + n)
+        ref, _ = oracle.attention_core(q[sl].astype(np.float64), k[sl].astype(np.float64),
+                                       v[sl].astype(np.float64), heads, None, oracle.chunk_allowed(n, chunk, rule))
+        err = np.abs(got[sl] - ref)
+        assert err.max() <= 1e-2 * max(1.0, np.abs(v).max()), (n, err.max())
+        cos = (got[sl] * ref).sum(1) / (np.linalg.norm(got[sl], axis=1) * np.linalg.norm(ref, axis=1))
+        assert cos.min() >= 0.9999, (n, cos.min())

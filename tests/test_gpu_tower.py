@@ -95,6 +95,24 @@ REDUCED = {
                                        stack=4), init="perturbed"),
     "fp32_stack4": reduced("tiny_fp32_b1", "fp32_stack4", dict(proj_hidden=128, proj_out=192, stack=4, batch=2),
                            init="perturbed"),
+    # chunked attention (1 s = 50 positions), chunk-causal, Whisper-medium width, pool 2, key mask over 3 clips
+    "chunk_causal_masked": reduced("whisper_medium_pool2_chunk1s_b16", "chunk_causal_masked",
+                                   dict(batch=3, n_layers=2, n_frames=900), init="perturbed"),
+    # block-diagonal chunks that do not divide the clip, ragged against the 128-query tiles
+    "chunk_block_ragged": reduced("whisper_large_b1", "chunk_block_ragged",
+                                  dict(batch=2, n_layers=2, n_frames=700, attn_chunk=37, attn_chunk_mode=2),
+                                  init="perturbed"),
+    # chunk of one position: block-diagonal attention returns each position's values
+    "chunk_block_one": reduced("whisper_large_b1", "chunk_block_one",
+                               dict(n_layers=1, n_frames=300, attn_chunk=1, attn_chunk_mode=2), init="perturbed"),
+    # chunk of one position, causal: ordinary causal attention
+    "chunk_causal_one": reduced("whisper_large_b1", "chunk_causal_one",
+                                dict(n_layers=1, n_frames=300, attn_chunk=1, attn_chunk_mode=1), init="sharp"),
+    # the fp32 path with chunk-causal attention and a key mask
+    "fp32_chunk_causal_masked": reduced("tiny_fp32_b1", "fp32_chunk_causal_masked",
+                                        dict(batch=3, attn_chunk=16, attn_chunk_mode=1), init="perturbed"),
+    "fp32_chunk_block": reduced("tiny_fp32_b1", "fp32_chunk_block", dict(attn_chunk=30, attn_chunk_mode=2),
+                                init="perturbed"),
 }
 
 
@@ -105,6 +123,8 @@ LENGTHS = {
     "fp32_perturbed_masked": [200, 137, 61],
     "stack4_masked": [900, 411, 101],
     "fp32_stack4": [200, 117],
+    "chunk_causal_masked": [900, 433, 97],
+    "fp32_chunk_causal_masked": [200, 137, 61],
 }
 
 
