@@ -55,10 +55,13 @@ __global__ __launch_bounds__(256) void attention_bf16_kernel(const bf16_t* __res
   __shared__ __align__(16) bf16_t Ks[2][ATT_BK * ATT_D];   // [key][dim], swizzled 16-byte chunks
   __shared__ __align__(16) bf16_t Vs[2][ATT_D * ATT_BK];   // [dim][key position], swizzled
 
-  const int b = blockIdx.z, h = blockIdx.y;
+  // RANGED: the grid is (head, clip, query block) with the query blocks in
+  // reverse, so the blocks that see the most keys (the last ones under the
+  // chunk-causal rule) are dispatched first and the short ones fill in behind.
+  const int b = RANGED ? blockIdx.y : blockIdx.z, h = RANGED ? blockIdx.x : blockIdx.y;
   const int start = starts[b];
   const int len = lens[b];
-  const int q0 = blockIdx.x * ATT_BQ;
+  const int q0 = (RANGED ? gridDim.z - 1 - blockIdx.z : blockIdx.x) * ATT_BQ;
   if (q0 >= len) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -168,14 +171,17 @@ __global__ __launch_bounds__(256) void attention_bf16_kernel(const bf16_t* __res
     }
     // lane holds keys 32 sub + 8 (v >> 2) + 4 hh + (v & 3) of query qi
     if (RANGED) {
-      const int first = k0 + 4 * hh;
+      // per-key masking only where the tile crosses some query's range edge
+      if (!__all(k0 >= k_lo && k0 + ATT_BK <= k_hi)) {
+        const int first = k0 + 4 * hh;
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
+        for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int key = first + 32 * sub + 8 * (v >> 2) + (v & 3);
-          if (key < k_lo || key >= k_hi) s[sub][v] = -INFINITY;
-        }
+          for (int v = 0; v < 16; ++v) {
+            const int key = first + 32 * sub + 8 * (v >> 2) + (v & 3);
+            if (key < k_lo || key >= k_hi) s[sub][v] = -INFINITY;
+          }
+      }
     } else if (RAGGED) {
       const int nvalid = len - k0 - 4 * hh;
 #pragma unroll
@@ -234,13 +240,15 @@ __global__ __launch_bounds__(256) void attention_bf16_kernel(const bf16_t* __res
   };
 
   if (RANGED) {
-    // every tile clamps its key rows and zeroes values past the clip
-    gload(kt_first * ATT_BK, std::true_type{});
+    // tiles that run past the clip clamp their key rows and zero their values
+    if ((kt_first + 1) * ATT_BK > len) gload(kt_first * ATT_BK, std::true_type{});
+    else gload(kt_first * ATT_BK, std::false_type{});
     lstore(0);
     __syncthreads();
     for (int kt = kt_first; kt < kt_last; ++kt) {
       const int buf = (kt - kt_first) & 1;
-      gload((kt + 1) * ATT_BK, std::true_type{});
+      if ((kt + 2) * ATT_BK > len) gload((kt + 1) * ATT_BK, std::true_type{});
+      else gload((kt + 1) * ATT_BK, std::false_type{});
       tile(buf, kt * ATT_BK, std::true_type{});
       lstore(buf ^ 1);
       __syncthreads();
@@ -289,8 +297,8 @@ hipError_t attention_bf16(const bf16_t* qk, int64_t ld_qk, const bf16_t* vt, int
   if (n_clips <= 0 || max_len <= 0 || n_heads <= 0 || (!key_lo != !key_hi)) return hipErrorInvalidValue;
   dim3 grid((max_len + ATT_BQ - 1) / ATT_BQ, n_heads, n_clips);
   if (key_lo)
-    hipLaunchKernelGGL(attention_bf16_kernel<true>, grid, dim3(256), 0, stream, qk, ld_qk, vt, ld_vt, start, len,
-                       n_heads * ATT_D, o, ld_o, key_lo, key_hi);
+    hipLaunchKernelGGL(attention_bf16_kernel<true>, dim3(n_heads, n_clips, grid.x), dim3(256), 0, stream, qk, ld_qk,
+                       vt, ld_vt, start, len, n_heads * ATT_D, o, ld_o, key_lo, key_hi);
   else
     hipLaunchKernelGGL(attention_bf16_kernel<false>, grid, dim3(256), 0, stream, qk, ld_qk, vt, ld_vt, start, len,
                        n_heads * ATT_D, o, ld_o, nullptr, nullptr);
