@@ -67,7 +67,8 @@ SIGNATURES = {
     # aenc_kernels.h
     "aenc_k_gemm_bf16": (c_int, [c_int, c_void_p, c_int64, c_void_p, c_void_p, c_void_p, c_int64, c_int, c_int,
                                  c_int, c_int, c_void_p]),
-    "aenc_k_qkv_bf16": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_int, c_int, c_void_p]),
+    "aenc_k_qkv_bf16": (c_int, [c_void_p, c_void_p, c_void_p, c_float, c_void_p, c_void_p, c_int64, c_int, c_int,
+                                c_void_p]),
     "aenc_k_attention_bf16": (c_int, [c_void_p, c_void_p, c_int64, c_void_p, c_void_p, c_int, c_int, c_int,
                                       c_void_p, c_void_p, c_void_p, c_void_p]),
     "aenc_k_chunk_ranges": (c_int, [c_void_p, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p,

@@ -76,7 +76,8 @@ __global__ __launch_bounds__(256) void attention_bf16_kernel(const bf16_t* __res
     kt_last = (key_hi[start + min(q0 + ATT_BQ, len) - 1] - 1) / ATT_BK;
   }
 
-  // Q fragments (B operand of S^T = K Q^T): dims 16s + 8hh .. +7.
+  // Q fragments (B operand of S^T = K Q^T): dims 16s + 8hh .. +7. Q arrives
+  // multiplied by log2(e)/sqrt(64), so scores are base-2 exponents.
   bf16x8 qf[4];
   {
     const bf16_t* qrow = qk + (int64_t)(start + min(qi, len - 1)) * ld_qk + h * ATT_D + 8 * hh;
@@ -85,35 +86,36 @@ __global__ __launch_bounds__(256) void attention_bf16_kernel(const bf16_t* __res
   }
 
   // Cooperative tile loads: two 16-byte chunks of K and two of V^T per thread.
-  const bf16_t* kbase = qk + d + h * ATT_D;
+  // Whole tiles come through buffer loads based at the clip's first row: the
+  // per-lane offset is fixed and the tile's key offset rides in the scalar
+  // offset, so a tile costs no address arithmetic. A tile that runs past the
+  // clip clamps its key rows (plain loads) and zeroes the values of keys past
+  // the clip (a zero probability times a non-finite value would still poison
+  // the sum).
+  const bf16_t* kbase = qk + (int64_t)start * ld_qk + d + h * ATT_D;
   const bf16_t* vbase = vt + (int64_t)(h * ATT_D) * ld_vt + start;
-  u32x4 rk[2], rv[2];
-  // RAGGED: the tile may run past the clip; key rows are clamped and the
-  // values of keys past the clip are zeroed (a zero probability times a
-  // non-finite value would still poison the sum).
-  // Per-lane chunk pointers for k0 = 0; a tile adds the uniform k0 offsets.
-  const bf16_t* kp[2];
-  const bf16_t* vp[2];
+  const __amdgpu_buffer_rsrc_t rsk = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(kbase), (short)0,
+                                                                       0x7fffffff, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsv = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(vbase), (short)0,
+                                                                       0x7fffffff, 0x00020000);
+  uint32_t koff[2], voff[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int c = tid + 256 * i;
-    kp[i] = kbase + (int64_t)(start + (c >> 3)) * ld_qk + (c & 7) * 8;
-    vp[i] = vbase + (int64_t)(c >> 3) * ld_vt + (c & 7) * 8;
+    koff[i] = (uint32_t)(((c >> 3) * ld_qk + (c & 7) * 8) * 2);
+    voff[i] = (uint32_t)(((c >> 3) * ld_vt + (c & 7) * 8) * 2);
   }
+  u32x4 rk[2], rv[2];
   auto gload = [&](int k0, auto ragged) {
     constexpr bool RAGGED = decltype(ragged)::value;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int c = tid + 256 * i;
       const int key = c >> 3, ch = c & 7;
-      if (RAGGED)
-        rk[i] = *(const u32x4*)(kbase + (int64_t)(start + min(k0 + key, len - 1)) * ld_qk + ch * 8);
-      else
-        rk[i] = *(const u32x4*)(kp[i] + (int64_t)k0 * ld_qk);
-      const int kc = c & 7;
-      u32x4 v = *(const u32x4*)(vp[i] + k0);
       if (RAGGED) {
-        const int first = k0 + kc * 8;
+        rk[i] = *(const u32x4*)(kbase + (int64_t)min(k0 + key, len - 1) * ld_qk + ch * 8);
+        u32x4 v = *(const u32x4*)(vbase + (int64_t)key * ld_vt + k0 + ch * 8);
+        const int first = k0 + ch * 8;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           uint32_t word = v[w];
@@ -121,8 +123,11 @@ __global__ __launch_bounds__(256) void attention_bf16_kernel(const bf16_t* __res
           if (first + 2 * w + 1 >= len) word &= 0x0000FFFFu;
           v[w] = word;
         }
+        rv[i] = v;
+      } else {
+        rk[i] = __builtin_amdgcn_raw_buffer_load_b128(rsk, koff[i], (uint32_t)(k0 * ld_qk * 2), 0);
+        rv[i] = __builtin_amdgcn_raw_buffer_load_b128(rsv, voff[i], (uint32_t)(k0 * 2), 0);
       }
-      rv[i] = v;
     }
   };
   auto lstore = [&](int buf) {
@@ -144,86 +149,99 @@ __global__ __launch_bounds__(256) void attention_bf16_kernel(const bf16_t* __res
     }
   };
 
-  const float c = 0.125f * 1.44269504088896341f;           // 1/sqrt(64) * log2(e)
-  const float slack = 8.0f / c;                              // 2^8 headroom, in score units
+  // Online softmax in base 2. m_run is the row's reference maximum; every
+  // tile's score accumulator starts at -m_run (negm), so the MFMAs produce
+  // s - m_run directly and p = 2^acc needs no per-score arithmetic. The
+  // reference moves (and the sums are rescaled) only when a row's tile maximum
+  // exceeds it by more than 2^8 in probability: until then the stale maximum
+  // scales every term of the row by the same factor (at most 256), which the
+  // final division by the row sum cancels.
+  constexpr float slack = 8.0f;
   float m_run = -INFINITY, l_run = 0.0f;
+  f32x16 negm;                                                // -m_run, or 0 before the first key
+#pragma unroll
+  for (int v = 0; v < 16; ++v) negm[v] = 0.0f;
   f32x16 oacc[2];
 #pragma unroll
   for (int es = 0; es < 2; ++es)
 #pragma unroll
     for (int v = 0; v < 16; ++v) oacc[es][v] = 0.0f;
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  // One 64-key tile from LDS buffer `buf`; RAGGED: keys past the clip are masked.
-  auto tile = [&](int buf, int k0, auto ragged) {
-    constexpr bool RAGGED = decltype(ragged)::value;
-    // ---- S^T = K Q^T for two 32-key sub-tiles ----
+  // One 64-key tile from LDS buffer `buf`; MASKED: keys past the clip (or, RANGED,
+  // outside the query's range) are masked.
+  auto tile = [&](int buf, int k0, auto masked) {
+    constexpr bool MASKED = decltype(masked)::value;
+    // ---- S^T - m_run = K Q^T - m_run for two 32-key sub-tiles ----
     f32x16 s[2];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) s[sub][v] = 0.0f;
       const int key = 32 * sub + fq;
+      s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          *(const bf16x8*)(&Ks[buf][key * ATT_D + att_swz(key, hh) * 8]), qf[0], negm, 0, 0, 0);
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
+      for (int st = 1; st < 4; ++st) {
         const bf16x8 kf = *(const bf16x8*)(&Ks[buf][key * ATT_D + att_swz(key, 2 * st + hh) * 8]);
         s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[st], s[sub], 0, 0, 0);
       }
     }
     // lane holds keys 32 sub + 8 (v >> 2) + 4 hh + (v & 3) of query qi
-    if (RANGED) {
+    if (MASKED) {
+      const int lo = RANGED ? k_lo : 0, hi = RANGED ? k_hi : len;
       // per-key masking only where the tile crosses some query's range edge
-      if (!__all(k0 >= k_lo && k0 + ATT_BK <= k_hi)) {
+      if (!__all(k0 >= lo && k0 + ATT_BK <= hi)) {
         const int first = k0 + 4 * hh;
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int key = first + 32 * sub + 8 * (v >> 2) + (v & 3);
-            if (key < k_lo || key >= k_hi) s[sub][v] = -INFINITY;
+            if (key < lo || key >= hi) s[sub][v] = -INFINITY;
           }
       }
-    } else if (RAGGED) {
-      const int nvalid = len - k0 - 4 * hh;
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-        for (int v = 0; v < 16; ++v)
-          if (32 * sub + 8 * (v >> 2) + (v & 3) >= nvalid) s[sub][v] = -INFINITY;
     }
     float mx = s[0][0];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
       for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[sub][v]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    // Rescale only when some row's maximum outgrew the reference by more than
-    // the slack (a uniform branch, rarely taken after the first tile).
-    if (__any(mx > m_run + slack)) {
-      const float m_new = fmaxf(m_run, mx);
-      // RANGED: a row may still have seen no key at all (both -inf)
-      const float alpha = (RANGED && m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f((m_run - m_new) * c);
-      m_run = m_new;
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));                  // the row's tile maximum, relative to m_run
+    // Move the reference when some row outgrew it by more than the slack, or
+    // sees its first key (a uniform branch, rarely taken after the first tile).
+    const bool fresh = m_run == -INFINITY;
+    if (__any(fresh ? mx > -INFINITY : mx > slack)) {
+      const float shift = fresh ? (mx == -INFINITY ? 0.0f : mx) : fmaxf(mx, 0.0f);
+      const float alpha = fresh ? 1.0f : __builtin_amdgcn_exp2f(-shift);
+      if (!(fresh && mx == -INFINITY)) m_run = fresh ? mx : m_run + shift;
       l_run *= alpha;
 #pragma unroll
       for (int es = 0; es < 2; ++es)
 #pragma unroll
         for (int v = 0; v < 16; ++v) oacc[es][v] *= alpha;
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s[sub][v] -= shift;
+      const float nm = m_run == -INFINITY ? 0.0f : -m_run;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) negm[v] = nm;
     }
-    const float mc = (RANGED && m_run == -INFINITY) ? 0.0f : m_run * c;
 
-    float lsum = 0.0f;
     bf16x8 pb[2][2];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[sub][8 * u + j], c, -mc));
-          lsum += p;
-          pb[sub][u][j] = (__bf16)p;
-        }
-    l_run += lsum;
+        for (int j = 0; j < 8; ++j) pb[sub][u][j] = (__bf16)__builtin_amdgcn_exp2f(s[sub][8 * u + j]);
+    // row sum of the rounded probabilities (the values P V multiplies), two per instruction
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int j = 0; j < 8; j += 2)
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[sub][u][j], pb[sub][u][j + 1]}, ones, l_run, false);
 
     // ---- O^T += V^T P^T ----
 #pragma unroll
@@ -239,40 +257,22 @@ __global__ __launch_bounds__(256) void attention_bf16_kernel(const bf16_t* __res
     }
   };
 
-  if (RANGED) {
-    // tiles that run past the clip clamp their key rows and zero their values
-    if ((kt_first + 1) * ATT_BK > len) gload(kt_first * ATT_BK, std::true_type{});
-    else gload(kt_first * ATT_BK, std::false_type{});
-    lstore(0);
+  // Tiles kt_first .. kt_last; a tile that runs past the clip is loaded ragged.
+  // Without ranges only the last tile can cross the clip's end (masked, peeled).
+  if ((kt_first + 1) * ATT_BK > len) gload(kt_first * ATT_BK, std::true_type{});
+  else gload(kt_first * ATT_BK, std::false_type{});
+  lstore(0);
+  __syncthreads();
+  for (int kt = kt_first; kt < kt_last; ++kt) {
+    const int buf = (kt - kt_first) & 1;
+    if ((kt + 2) * ATT_BK > len) gload((kt + 1) * ATT_BK, std::true_type{});
+    else gload((kt + 1) * ATT_BK, std::false_type{});
+    if (RANGED) tile(buf, kt * ATT_BK, std::true_type{});
+    else tile(buf, kt * ATT_BK, std::false_type{});
+    lstore(buf ^ 1);
     __syncthreads();
-    for (int kt = kt_first; kt < kt_last; ++kt) {
-      const int buf = (kt - kt_first) & 1;
-      if ((kt + 2) * ATT_BK > len) gload((kt + 1) * ATT_BK, std::true_type{});
-      else gload((kt + 1) * ATT_BK, std::false_type{});
-      tile(buf, kt * ATT_BK, std::true_type{});
-      lstore(buf ^ 1);
-      __syncthreads();
-    }
-    tile((kt_last - kt_first) & 1, kt_last * ATT_BK, std::true_type{});
-  } else {
-    const int n_tiles = kt_last + 1;
-    if (n_tiles == 1) gload(0, std::true_type{});
-    else gload(0, std::false_type{});
-    lstore(0);
-    __syncthreads();
-    // full tiles: prefetch the next tile into registers while this one computes
-    for (int kt = 0; kt + 1 < n_tiles; ++kt) {
-      const int buf = kt & 1;
-      const int k0 = kt * ATT_BK;
-      if (kt + 2 == n_tiles) gload(k0 + ATT_BK, std::true_type{});
-      else gload(k0 + ATT_BK, std::false_type{});
-      tile(buf, k0, std::false_type{});
-      lstore(buf ^ 1);
-      __syncthreads();
-    }
-    // the last tile may be ragged
-    tile((n_tiles - 1) & 1, (n_tiles - 1) * ATT_BK, std::true_type{});
   }
+  tile((kt_last - kt_first) & 1, kt_last * ATT_BK, std::true_type{});
 
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = 1.0f / l_tot;
@@ -295,6 +295,9 @@ hipError_t attention_bf16(const bf16_t* qk, int64_t ld_qk, const bf16_t* vt, int
                           const int32_t* len, int n_clips, int max_len, int n_heads, bf16_t* o, int64_t ld_o,
                           const int32_t* key_lo, const int32_t* key_hi, hipStream_t stream) {
   if (n_clips <= 0 || max_len <= 0 || n_heads <= 0 || (!key_lo != !key_hi)) return hipErrorInvalidValue;
+  // buffer-load offsets within one clip stay below 2^31 bytes
+  if ((int64_t)(max_len + ATT_BK) * ld_qk * 2 >= INT32_MAX || (int64_t)ATT_D * ld_vt * 2 >= INT32_MAX)
+    return hipErrorInvalidValue;
   dim3 grid((max_len + ATT_BQ - 1) / ATT_BQ, n_heads, n_clips);
   if (key_lo)
     hipLaunchKernelGGL(attention_bf16_kernel<true>, dim3(n_heads, n_clips, grid.x), dim3(256), 0, stream, qk, ld_qk,

@@ -61,10 +61,12 @@ struct EpiParams {
   const float* bias;   // [N] or null
   void* c;             // output base (element type by kind)
   RowMap crow;         // C row addressing
-  // EPI_QKV_BF16
+  // EPI_QKV_BF16: columns n < q_cols (Q) are multiplied by q_scale after the bias
   int n_split;
   bf16_t* vt;
   int64_t ld_vt;
+  int q_cols;
+  float q_scale;
   // EPI_GELU_PE_F32
   const float* pe;
   int pe_period;
@@ -119,6 +121,7 @@ struct Epilogue {
       }
       return;
     }
+    if (EPI == EPI_QKV_BF16 && n < p.q_cols) v *= p.q_scale;
     if (ro.o[0] >= 0) one(p, ro.o[0], ro.t[0], n, v.x);
     if (ro.o[1] >= 0) one(p, ro.o[1], ro.t[1], n, v.y);
     if (ro.o[2] >= 0) one(p, ro.o[2], ro.t[2], n, v.z);
@@ -176,6 +179,9 @@ struct Epilogue {
       if (p.bias && n < N) {
         const float4 b = *(const float4*)(p.bias + n);
         v.x += b.x; v.y += b.y; v.z += b.z; v.w += b.w;
+      }
+      if (EPI == EPI_QKV_BF16 && n < p.q_cols) {
+        v.x *= p.q_scale; v.y *= p.q_scale; v.z *= p.q_scale; v.w *= p.q_scale;
       }
       if (EPI == EPI_GELU_PE_F32 && o >= 0) {
         const float4 pe = *(const float4*)(p.pe + (int64_t)(r % p.pe_period) * p.pe_ld + n);

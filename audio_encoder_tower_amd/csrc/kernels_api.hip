@@ -1,4 +1,5 @@
 // C entry points of include/aenc_kernels.h: host-side checks, then one launch.
+#include <cmath>
 #include <cstdio>
 #include <string>
 
@@ -50,11 +51,14 @@ extern "C" int aenc_k_gemm_bf16(int epi, const void* A, int64_t lda, const void*
                               tile, (hipStream_t)stream), "gemm");
 }
 
-extern "C" int aenc_k_qkv_bf16(const void* A, const void* Wqkv, const float* bias, void* qk, void* vt,
-                               int64_t ld_vt, int M, int d, void* stream) {
+extern "C" int aenc_k_qkv_bf16(const void* A, const void* Wqkv, const float* bias, float q_scale, void* qk,
+                               void* vt, int64_t ld_vt, int M, int d, void* stream) {
   if (!A || !Wqkv || !qk || !vt) return fail("NULL operand");
   if (M < 1 || d < 64 || d % 64 || ld_vt < M + 64 || ld_vt % 8) return fail("bad QKV sizes");
+  if (!(q_scale > 0.0f) || !std::isfinite(q_scale)) return fail("q_scale must be positive and finite");
   EpiParams ep{};
+  ep.q_cols = q_scale == 1.0f ? 0 : d;
+  ep.q_scale = q_scale;
   ep.bias = bias;
   ep.c = qk;
   ep.crow = dense_rows(2 * d);

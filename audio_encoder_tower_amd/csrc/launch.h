@@ -23,8 +23,11 @@ hipError_t gemm_f32(int epi, const float* A, RowMap arow, const float* W, int64_
 // column h*64 and K at column d + h*64; vt: V transposed, row (h*64 + e) holds
 // feature e of head h for every packed row, ld_vt apart. Clip b owns packed rows
 // [start[b], start[b] + len[b]); start[b] % 8 == 0. o: [rows, ld_o] bf16, head h at column h*64.
+// Q must arrive multiplied by ATT_Q_SCALE = log2(e)/sqrt(64), so that Q K^T is
+// the softmax exponent in base 2 (the QKV epilogue applies it).
 // key_lo/key_hi (both or neither): per packed row, the clip-relative keys
 // [key_lo, key_hi) it sees, non-empty and non-decreasing along the clip.
+constexpr float ATT_Q_SCALE = 0.18033688011112042f;
 hipError_t attention_bf16(const bf16_t* qk, int64_t ld_qk, const bf16_t* vt, int64_t ld_vt,
                           const int32_t* start, const int32_t* len, int n_clips, int max_len, int n_heads,
                           bf16_t* o, int64_t ld_o, const int32_t* key_lo, const int32_t* key_hi,

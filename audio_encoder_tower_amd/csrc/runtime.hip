@@ -672,6 +672,8 @@ extern "C" int aenc_forward(aenc_handle* h, const void* mel, const uint8_t* mask
       eq.n_split = 2 * d;
       eq.vt = (bf16_t*)h->vt;
       eq.ld_vt = h->ld_vt;
+      eq.q_cols = d;                 // the attention kernel takes Q in base-2 score units
+      eq.q_scale = ATT_Q_SCALE;
       e = gemm_bf16(EPI_QKV_BF16, (const bf16_t*)h->a, dense_d, (const bf16_t*)L.qkv_w, d, M_rows, 3 * d, d, mv, eq,
                     pick_tile(M_rows, 3 * d), s);
     } else {

@@ -41,11 +41,15 @@ def gemm_bf16(epi: str, a: torch.Tensor, w: torch.Tensor, bias: Optional[torch.T
     return c
 
 
+# Q scale the attention kernel expects: log2(e) / sqrt(64) (scores as base-2 exponents).
+ATTN_Q_SCALE = 0.18033688011112042
+
+
 def qkv_bf16(a: torch.Tensor, wqkv: torch.Tensor, bias: Optional[torch.Tensor], qk: torch.Tensor,
-             vt: torch.Tensor) -> None:
+             vt: torch.Tensor, q_scale: float = 1.0) -> None:
     M, d = a.shape
     assert wqkv.shape == (3 * d, d) and qk.shape == (M, 2 * d) and vt.shape[0] == d
-    check(lib().aenc_k_qkv_bf16(_p(a), _p(wqkv), _p(bias), _p(qk), _p(vt), vt.shape[1], M, d, _s()),
+    check(lib().aenc_k_qkv_bf16(_p(a), _p(wqkv), _p(bias), q_scale, _p(qk), _p(vt), vt.shape[1], M, d, _s()),
           "aenc_k_qkv_bf16")
 
 

@@ -42,16 +42,22 @@ enum { AENC_TILE_256x256 = 0, AENC_TILE_128x128 = 1 };
 int aenc_k_gemm_bf16(int epi, const void *A, int64_t lda, const void *W, const float *bias, void *C,
                      int64_t ldc, int M, int N, int K, int tile, void *stream);
 
+/* Scale of Q that aenc_k_attention_bf16 expects: log2(e) / sqrt(64), which
+ * makes Q K^T the softmax exponent in base 2. */
+#define AENC_ATTN_Q_SCALE 0.18033688011112042f
+
 /* The QKV projection of a block: [Q | K | V] = A Wqkv^T + bqkv with A bf16
- * [M, d], Wqkv bf16 [3d, d], bias fp32 [3d] or NULL. Q and K go to qk (bf16
- * [M, 2d]); V goes transposed to vt (bf16, row e of [d, ld_vt] holds feature
- * e of every row; ld_vt >= M + 64, a multiple of 8). d = 64 * heads. */
-int aenc_k_qkv_bf16(const void *A, const void *Wqkv, const float *bias, void *qk, void *vt, int64_t ld_vt,
-                    int M, int d, void *stream);
+ * [M, d], Wqkv bf16 [3d, d], bias fp32 [3d] or NULL; the Q columns are then
+ * multiplied by q_scale (> 0; 1 for plain Q, AENC_ATTN_Q_SCALE for the input
+ * of aenc_k_attention_bf16) before rounding. Q and K go to qk (bf16 [M, 2d]);
+ * V goes transposed to vt (bf16, row e of [d, ld_vt] holds feature e of every
+ * row; ld_vt >= M + 64, a multiple of 8). d = 64 * heads. */
+int aenc_k_qkv_bf16(const void *A, const void *Wqkv, const float *bias, float q_scale, void *qk, void *vt,
+                    int64_t ld_vt, int M, int d, void *stream);
 
 /* Bidirectional attention over packed clips: clip b owns rows
- * [start[b], start[b] + len[b]) of qk (Q of head h at column 64h, K at column
- * d + 64h) and the same columns of vt; every start[b] must be a multiple of 8,
+ * [start[b], start[b] + len[b]) of qk (Q of head h at column 64h, multiplied
+ * by AENC_ATTN_Q_SCALE; K at column d + 64h) and the same columns of vt; every start[b] must be a multiple of 8,
  * every len[b] >= 1 and max_len >= the longest clip; vt must hold 64 columns
  * past the end of the last clip. out: bf16 [rows, d], head h at column 64h;
  * rows outside every clip are not written.

@@ -36,6 +36,17 @@ def host(t):
     return t.float().cpu().numpy().astype(np.float64)
 
 
+ATTN_Q_SCALE = 0.18033688011112042   # log2(e) / sqrt(64): the attention kernel's Q units
+
+
+def scaled_q(q):
+    """Q as the attention kernel sees it: q * ATTN_Q_SCALE rounded to bf16,
+    returned divided back (float64) for the oracle; the device gets
+    exactly q_back * ATTN_Q_SCALE (= the rounded value, up to float64)."""
+    qs = synth.round_to_bf16((q * ATTN_Q_SCALE).astype(np.float32)).astype(np.float64)
+    return qs / ATTN_Q_SCALE
+
+
 GEMM_SHAPES = [
     (300, 384, 320),      # ragged M and N against every tile shape
     (64, 64, 64),
@@ -77,7 +88,8 @@ def test_gemm_bf16(_lib, shape, epi, tile):
         np.testing.assert_allclose(got, ref, rtol=1e-5, atol=2e-6 * scale)
 
 
-def test_qkv_split_layout(_lib):
+@pytest.mark.parametrize("q_scale", [1.0, 0.18033688011112042], ids=["plain", "attention_q_scale"])
+def test_qkv_split_layout(_lib, q_scale):
     rng = np.random.default_rng(1)
     M, d = 777, 256
     a = bf16(rng, M, d)
@@ -86,9 +98,10 @@ def test_qkv_split_layout(_lib):
     ld_vt = (M + 63) // 64 * 64 + 64
     qk = torch.empty(M, 2 * d, device=DEV, dtype=torch.bfloat16)
     vt = torch.zeros(d, ld_vt, device=DEV, dtype=torch.bfloat16)
-    _lib.steps.qkv_bf16(dev_bf16(a), dev_bf16(wqkv), dev_f32(bias), qk, vt)
+    _lib.steps.qkv_bf16(dev_bf16(a), dev_bf16(wqkv), dev_f32(bias), qk, vt, q_scale=q_scale)
     torch.cuda.synchronize()
     ref = oracle.linear(a.astype(np.float64), wqkv.astype(np.float64), bias.astype(np.float64))
+    ref[:, :d] *= q_scale                         # Q columns only
     np.testing.assert_allclose(host(qk), ref[:, :2 * d], rtol=2 ** -8, atol=1e-4)
     np.testing.assert_allclose(host(vt)[:, :M], ref[:, 2 * d:].T, rtol=2 ** -8, atol=1e-4)
     assert np.all(host(vt)[:, M:] == 0)
@@ -192,8 +205,9 @@ def test_attention_bf16(_lib, lens, heads, scale):
         starts.append((starts[-1] + n + 7) // 8 * 8)
     rows = starts[-1] + lens[-1]
     q, k, v = (bf16(rng, rows, d, scale=scale) for _ in range(3))
+    q = scaled_q(q)
     ld_vt = (rows + 63) // 64 * 64 + 64
-    qk = np.concatenate([q, k], axis=1)
+    qk = np.concatenate([q * ATTN_Q_SCALE, k], axis=1)
     vt = np.zeros((d, ld_vt), np.float32)
     vt[:, :rows] = v.T
     st = torch.tensor(starts, dtype=torch.int32, device=DEV)
@@ -289,8 +303,9 @@ def test_attention_bf16_chunked(_lib, lens, heads, chunk, mode):
     key_hi = torch.zeros(rows + 8, dtype=torch.int32, device=DEV)
     _lib.steps.chunk_ranges(md, B, T, chunk, mode, rm, cu_d, key_lo, key_hi)
     q, k, v = (bf16(rng, rows, d, scale=1.5) for _ in range(3))
+    q = scaled_q(q)
     ld_vt = (rows + 63) // 64 * 64 + 64
-    qk = np.concatenate([q, k], axis=1)
+    qk = np.concatenate([q * ATTN_Q_SCALE, k], axis=1)
     vt = np.zeros((d, ld_vt), np.float32)
     vt[:, :rows] = v.T
     out = torch.full((rows, d), float("nan"), device=DEV, dtype=torch.bfloat16)
