@@ -91,10 +91,10 @@ def cpu_baseline(w, blocks: int = 0):
 
 # Kernel sources whose change invalidates stored hardware-counter readings.
 KERNEL_SOURCES = {
-    kind: ["gemm_bf16.hip", "epilogue.h", "common.h", "runtime.hip"]
+    kind: ["gemm_bf16.hip", "epilogue.h", "common.h", "launch.h"]
     for kind in ("qkv", "o_proj", "fc1", "fc2", "proj1", "proj2")
 }
-KERNEL_SOURCES["attention"] = ["attention.hip", "common.h", "runtime.hip"]
+KERNEL_SOURCES["attention"] = ["attention.hip", "common.h", "launch.h"]
 
 
 def source_digest(kind: str) -> str:
