@@ -99,9 +99,9 @@ extern "C" int aenc_cache_contains(aenc_cache* c, uint64_t key) {
   return c->index.count(key) ? 1 : 0;
 }
 
-extern "C" int aenc_cache_lookup(aenc_cache* c, uint64_t key, void* dst, void* stream) {
-  if (!c || !dst) { cache_error("cache and dst must not be NULL"); return AENC_E_INVAL; }
-  std::lock_guard<std::mutex> g(c->mu);
+namespace {
+// Lookup with the cache's mutex held: 1 hit (copy enqueued), 0 miss, < 0 error.
+int lookup_locked(aenc_cache* c, uint64_t key, void* dst, hipStream_t stream) {
   auto it = c->index.find(key);
   if (it == c->index.end()) {
     ++c->misses;
@@ -109,10 +109,17 @@ extern "C" int aenc_cache_lookup(aenc_cache* c, uint64_t key, void* dst, void* s
   }
   const int64_t slot = it->second;
   touch(c, slot);
-  const hipError_t e = slot_copy(c, slot, dst, c->pool + slot * c->entry_bytes, (hipStream_t)stream);
+  const hipError_t e = slot_copy(c, slot, dst, c->pool + slot * c->entry_bytes, stream);
   if (e != hipSuccess) { cache_error(hipGetErrorString(e)); return AENC_E_HIP; }
   ++c->hits;
   return 1;
+}
+}  // namespace
+
+extern "C" int aenc_cache_lookup(aenc_cache* c, uint64_t key, void* dst, void* stream) {
+  if (!c || !dst) { cache_error("cache and dst must not be NULL"); return AENC_E_INVAL; }
+  std::lock_guard<std::mutex> g(c->mu);
+  return lookup_locked(c, key, dst, (hipStream_t)stream);
 }
 
 extern "C" int aenc_cache_insert(aenc_cache* c, uint64_t key, const void* src, void* stream) {
@@ -165,14 +172,19 @@ extern "C" int aenc_forward_cached(aenc_handle* h, aenc_cache* c, const uint64_t
   const int64_t clip_bytes = shape[1] * shape[2] * (g.out_dtype == AENC_BF16 ? 2 : 4);
   if (clip_bytes != c->entry_bytes) { cache_error("cache entry size differs from one clip's output"); return AENC_E_INVAL; }
   int n_hit = 0;
-  for (int b = 0; b < g.batch; ++b) n_hit += aenc_cache_contains(c, keys[b]) == 1;
-  if (n_hit == g.batch) {                   // every clip cached: copies only
-    for (int b = 0; b < g.batch; ++b) {
-      const int st = aenc_cache_lookup(c, keys[b], (char*)out + b * clip_bytes, stream);
-      if (st < 0) return st;
+  {
+    // Decide and copy under one hold of the lock, so that no other thread can
+    // evict an entry between the check and its copy.
+    std::lock_guard<std::mutex> lk(c->mu);
+    for (int b = 0; b < g.batch; ++b) n_hit += c->index.count(keys[b]) ? 1 : 0;
+    if (n_hit == g.batch) {                 // every clip cached: copies only
+      for (int b = 0; b < g.batch; ++b) {
+        const int st = lookup_locked(c, keys[b], (char*)out + b * clip_bytes, (hipStream_t)stream);
+        if (st < 0) return st;
+      }
+      if (hits) *hits = n_hit;
+      return AENC_OK;
     }
-    if (hits) *hits = n_hit;
-    return AENC_OK;
   }
   // Any miss runs the whole batch (its shape is fixed), then stores the new clips.
   const int st = aenc_forward(h, mel, mask, out, stream);
