@@ -113,6 +113,14 @@ REDUCED = {
                                         dict(batch=3, attn_chunk=16, attn_chunk_mode=1), init="perturbed"),
     "fp32_chunk_block": reduced("tiny_fp32_b1", "fp32_chunk_block", dict(attn_chunk=30, attn_chunk_mode=2),
                                 init="perturbed"),
+    # degenerate sizes: two mel frames -> one position; four frames pooled into one output row
+    "one_position": reduced("whisper_large_b1", "one_position", dict(batch=3, n_layers=2, n_frames=2),
+                            init="perturbed"),
+    "pool_one_output": reduced("whisper_medium_pool2_b1", "pool_one_output", dict(batch=2, n_layers=1, n_frames=4),
+                               init="perturbed"),
+    "projector_one_position": reduced("whisper_large_b1", "projector_one_position",
+                                      dict(n_layers=1, n_frames=2, proj_hidden=3072, proj_out=3072),
+                                      init="perturbed"),
 }
 
 
