@@ -143,9 +143,9 @@ aenc_handle *aenc_create(const aenc_geometry *g, const aenc_weights *w);
  *   mel  : device, [batch, n_mel, n_frames], dtype. Row-major, channels first.
  *   mask : device uint8 [batch, T] key-padding mask (1 = valid position) or
  *          NULL (all valid). Masked positions take no part as keys; their own
- *          output rows are written as zeros. Every clip needs at least one
- *          valid position (otherwise its rows are unspecified). Frames that
- *          only masked positions read may hold anything finite.
+ *          output rows are written as zeros, so a clip with no valid
+ *          position at all comes out as zeros. Frames that only masked
+ *          positions read may hold anything finite.
  *   out  : device, [batch, T_out, D_out] in out_dtype, with T_out = T /
  *          pool_step and D_out = proj_out or d_model (see aenc_output_shape).
  * Forwards on one handle share its workspace and must be ordered (one stream

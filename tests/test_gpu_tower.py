@@ -113,6 +113,10 @@ REDUCED = {
                                         dict(batch=3, attn_chunk=16, attn_chunk_mode=1), init="perturbed"),
     "fp32_chunk_block": reduced("tiny_fp32_b1", "fp32_chunk_block", dict(attn_chunk=30, attn_chunk_mode=2),
                                 init="perturbed"),
+    # a clip with no valid position at all (its rows come out as zeros), with the projector
+    "empty_clip_masked": reduced("whisper_large_b1", "empty_clip_masked",
+                                 dict(batch=3, n_layers=1, n_frames=400, d_model=256, n_heads=4, d_ffn=1024,
+                                      proj_hidden=512, proj_out=384), init="perturbed"),
     # degenerate sizes: two mel frames -> one position; four frames pooled into one output row
     "one_position": reduced("whisper_large_b1", "one_position", dict(batch=3, n_layers=2, n_frames=2),
                             init="perturbed"),
@@ -132,6 +136,7 @@ LENGTHS = {
     "stack4_masked": [900, 411, 101],
     "fp32_stack4": [200, 117],
     "chunk_causal_masked": [900, 433, 97],
+    "empty_clip_masked": [400, 0, 51],
     "fp32_chunk_causal_masked": [200, 137, 61],
 }
 
