@@ -5,7 +5,8 @@
 // ENCODER: single bidirectional pass; "Voxtral-Mini-3B-2507", (1) AUDIO
 // ENCODER: 20 heads and 20 KV heads, head_dim 64). Clips are packed: clip b
 // owns rows [start[b], start[b] + len[b]) and masked positions were removed
-// beforehand, so the only masking left is the ragged end of each clip.
+// beforehand, so the only masking left is the ragged end of each clip, or,
+// for chunked attention, each query's key range.
 //
 // bf16 kernel (flash-style, one pass over the keys with an online softmax):
 //   - workgroup = (128-query tile, head, clip), four wave64s with 32 queries each;
@@ -16,8 +17,10 @@
 //     and row sum need one cross-lane exchange per tile, not a tree;
 //   - P^T in registers is exactly the B operand of O^T = V^T P^T, so P never
 //     goes through LDS; V^T's keys are stored in the order that matches;
-//   - scores are scaled by 1/sqrt(64) and turned into base-2 exponents in a
-//     single fma; softmax statistics and the output accumulate in fp32;
+//   - Q arrives pre-scaled by log2(e)/sqrt(64) (the QKV epilogue applies it
+//     before rounding), and each tile's score accumulator starts at minus the
+//     row's reference maximum, so the MFMAs yield base-2 exponents ready for
+//     v_exp_f32; softmax statistics and the output accumulate in fp32;
 //   - the running maximum is moved (and the sums rescaled) only when a row's
 //     tile maximum exceeds it by more than 2^8 in probability: until then the
 //     stale maximum only scales every term of the row by the same factor
