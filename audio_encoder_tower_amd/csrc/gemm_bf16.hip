@@ -42,7 +42,7 @@
 namespace aenc {
 
 constexpr int GEMM_BK = 64;
-constexpr int GEMM_GROUP_M = 8;
+constexpr int GEMM_GROUP_M = 4;
 constexpr int N_XCD = 8;
 
 struct GemmArgs {
