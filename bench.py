@@ -31,6 +31,7 @@ METRIC = "encoder audio-seconds/sec (30 s chunks, bf16, 1 GPU) + % of bf16 MFMA 
 # MI355X published peaks: dense bf16 MFMA 2.5 PFLOP/s, fp32 157.3 TFLOP/s, HBM3E 8 TB/s.
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
+PEAK_F32_VALU_NOPK = 78.6   # fp32 vector FMA without packed math (packed math is off in this build)
 
 
 def step_flops(g, kind: str, rows: int, proj_rows: int) -> float:
@@ -142,9 +143,41 @@ def frontend_leg(batch: int, steps: int):
     frames = batch * (n // 160)
     dft_flops = 2.0 * frames * 404 * 400
     mel_flops = 2.0 * frames * 128 * 208
+    tf = (dft_flops + mel_flops) / (ms * 1e-3) / 1e12
     return {"workload": f"{batch} clips of 30 s, 16 kHz -> [{batch}, 128, 3000] bf16", "ms_per_batch": round(ms, 4),
             "audio_s_per_s": round(batch * 30.0 / (ms * 1e-3), 1),
-            "fp32_tflops": round((dft_flops + mel_flops) / (ms * 1e-3) / 1e12, 2)}
+            "fp32_tflops": round(tf, 2),
+            # fp32 GEMMs on the vector ALUs without packed math: 256 CUs x 64 lanes x 2 FLOP x 2.4 GHz
+            "roofline": {"bound": "alu", "achieved": round(tf, 2), "peak": PEAK_F32_VALU_NOPK, "unit": "TFLOP/s",
+                         "frac": round(tf / PEAK_F32_VALU_NOPK, 4)}}
+
+
+def cache_leg(enc, mel, mask, out, audio_s: float, steps: int):
+    """The embeddings cache on the bench batch: one forward that fills it (all
+    misses), then all-hit batches served by device copies."""
+    import torch
+    import audio_encoder_tower_amd as aenc
+    g = enc.geom
+    cache = aenc.EmbeddingsCache.for_encoder(enc, 2 * g.batch)
+    keys = list(range(1000, 1000 + g.batch))
+    stream = torch.cuda.current_stream()
+    start, mid, end = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    torch.cuda.synchronize()
+    start.record(stream)
+    _, hits0 = enc.forward_cached(cache, keys, mel, mask, out, stream)
+    mid.record(stream)
+    for _ in range(steps):
+        _, hits = enc.forward_cached(cache, keys, mel, mask, out, stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    miss_ms, hit_ms = start.elapsed_time(mid), mid.elapsed_time(end) / steps
+    nbytes = out.numel() * out.element_size()
+    stats = cache.stats()
+    cache.close()
+    return {"entries": g.batch, "entry_bytes": nbytes // g.batch, "first_batch_hits": hits0, "hits_per_batch": hits,
+            "miss_batch_ms": round(miss_ms, 3), "hit_batch_ms": round(hit_ms, 4),
+            "hit_copy_gbs": round(2 * nbytes / (hit_ms * 1e-3) / 1e9, 1),
+            "hit_audio_s_per_s": round(audio_s / (hit_ms * 1e-3), 1), "stats": stats}
 
 
 def side_stream_leg(enc, mel, mask, out, audio_s: float, n_enc: int = 4, gate_forwards: int = 3, shape=None,
@@ -371,6 +404,7 @@ def main():
         result["frontend"] = frontend_leg(g.batch, args.steps)
     if not args.no_side_stream:
         result["side_stream"] = side_stream_leg(enc, mel, mask, out, audio_s)
+        result["cache"] = cache_leg(enc, mel, mask, out, audio_s, args.steps)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_blocks)
     print(json.dumps(result), flush=True)
