@@ -27,7 +27,9 @@
 //    waves run a burst of 16 MFMAs at raised priority, the other group's
 //    waves, on the same SIMDs, read their next fragments from LDS and issue
 //    the copies of the next slice; a workgroup barrier ends each phase. One
-//    workgroup per CU (128 KiB of LDS). Used for the large GEMMs.
+//    workgroup per CU (128 KiB of LDS). Used for the large GEMMs. A variant
+//    for long K and narrow N gives A three LDS buffers (160 KiB in all), so
+//    A slices are requested two slices ahead.
 //  * 128x128, 4 waves, each wave 64x64, two workgroups per CU that overlap
 //    each other's copies and MFMAs. Used when the 256x256 tiles would leave
 //    most CUs idle (short batches).
@@ -336,6 +338,54 @@ __device__ __forceinline__ void read_half(const bf16_t* as, const bf16_t* bs, in
   read_frags<SN>(bs, b_row0, (4 * h + 2 + fk) ^ sw, fb[1]);
 }
 
+typedef int i32x4_asm __attribute__((ext_vector_type(4)));
+
+// read_half plus the wait for it, as one asm block: the compiler's wait
+// insertion then never sees these LDS reads, so it does not make them wait for
+// the direct-to-LDS copies in flight (it cannot tell that those target other
+// buffers once there are more than two).
+template <int SM, int SN>
+__device__ __forceinline__ void read_half_wait(const bf16_t* as, const bf16_t* bs, int a_row0, int b_row0, int sw,
+                                               int fk, int h, bf16x8 (&fa)[2][SM], bf16x8 (&fb)[2][SN]) {
+  static_assert(SM == 2 && SN == 4, "written for the 64x128 wave tile");
+  const uint32_t ab = (uint32_t)(uintptr_t)(lds_void*)as, bb = (uint32_t)(uintptr_t)(lds_void*)bs;
+  const uint32_t pa0 = ab + (a_row0 * GEMM_BK + ((4 * h + 0 + fk) ^ sw) * 8) * 2;
+  const uint32_t pa1 = ab + (a_row0 * GEMM_BK + ((4 * h + 2 + fk) ^ sw) * 8) * 2;
+  const uint32_t pb0 = bb + (b_row0 * GEMM_BK + ((4 * h + 0 + fk) ^ sw) * 8) * 2;
+  const uint32_t pb1 = bb + (b_row0 * GEMM_BK + ((4 * h + 2 + fk) ^ sw) * 8) * 2;
+  i32x4_asm r[12];
+  asm volatile(
+      "ds_read_b128 %0, %12\n"
+      "ds_read_b128 %1, %12 offset:4096\n"
+      "ds_read_b128 %2, %13\n"
+      "ds_read_b128 %3, %13 offset:4096\n"
+      "ds_read_b128 %4, %13 offset:8192\n"
+      "ds_read_b128 %5, %13 offset:12288\n"
+      "ds_read_b128 %6, %14\n"
+      "ds_read_b128 %7, %14 offset:4096\n"
+      "ds_read_b128 %8, %15\n"
+      "ds_read_b128 %9, %15 offset:4096\n"
+      "ds_read_b128 %10, %15 offset:8192\n"
+      "ds_read_b128 %11, %15 offset:12288\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7]),
+        "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11])
+      : "v"(pa0), "v"(pb0), "v"(pa1), "v"(pb1)
+      : "memory");
+  fa[0][0] = __builtin_bit_cast(bf16x8, r[0]);
+  fa[0][1] = __builtin_bit_cast(bf16x8, r[1]);
+  fb[0][0] = __builtin_bit_cast(bf16x8, r[2]);
+  fb[0][1] = __builtin_bit_cast(bf16x8, r[3]);
+  fb[0][2] = __builtin_bit_cast(bf16x8, r[4]);
+  fb[0][3] = __builtin_bit_cast(bf16x8, r[5]);
+  fa[1][0] = __builtin_bit_cast(bf16x8, r[6]);
+  fa[1][1] = __builtin_bit_cast(bf16x8, r[7]);
+  fb[1][0] = __builtin_bit_cast(bf16x8, r[8]);
+  fb[1][1] = __builtin_bit_cast(bf16x8, r[9]);
+  fb[1][2] = __builtin_bit_cast(bf16x8, r[10]);
+  fb[1][3] = __builtin_bit_cast(bf16x8, r[11]);
+}
+
 template <int SM, int SN>
 __device__ __forceinline__ void compute_half(f32x16 (&acc)[SM][SN], const bf16x8 (&fa)[2][SM],
                                              const bf16x8 (&fb)[2][SN]) {
@@ -349,14 +399,24 @@ struct BigCopy {
   __amdgpu_buffer_rsrc_t ra, rw;
   CopyPlan<4> pa, pw;
   int wave;
-  // this wave's 8 copy instructions of the slice at K byte offset k_bytes
-  __device__ __forceinline__ void slice(uint32_t k_bytes, bf16_t* la, bf16_t* lw) const {
+  // this wave's 4 copy instructions of the A (or W) part of the slice at K byte offset k_bytes
+  __device__ __forceinline__ void slice_a(uint32_t k_bytes, bf16_t* la) const {
 #pragma unroll
     for (int i = 0; i < 4; ++i) copy16(ra, la + (wave * 4 + i) * 8 * GEMM_BK, pa.off[i], k_bytes);
+  }
+  __device__ __forceinline__ void slice_w(uint32_t k_bytes, bf16_t* lw) const {
 #pragma unroll
     for (int i = 0; i < 4; ++i) copy16(rw, lw + (wave * 4 + i) * 8 * GEMM_BK, pw.off[i], k_bytes);
   }
+  // both parts: this wave's 8 copy instructions
+  __device__ __forceinline__ void slice(uint32_t k_bytes, bf16_t* la, bf16_t* lw) const {
+    slice_a(k_bytes, la);
+    slice_w(k_bytes, lw);
+  }
 };
+
+// vmcnt(4): everything but this wave's 4 most recent copies has landed.
+__device__ __forceinline__ void wait_copies_but4() { __builtin_amdgcn_s_waitcnt(0x3f74); }
 
 // One K slice in four phases, each closed by a workgroup barrier. Group 0
 // reads fragments (half 0, then half 1) in phases 0 and 2 and multiplies in
@@ -477,8 +537,147 @@ __global__ __launch_bounds__(BIG_THREADS) void gemm_bf16_256_kernel(GemmArgs g) 
 }
 
 // ---------------------------------------------------------------------------
+// 256x256 tiles with a deeper A prefetch, for long K and narrow N (the FFN's
+// second product). The same 8-wave ping-pong, but A slices run through three
+// LDS buffers and W slices through two (160 KiB): as each group starts reading
+// slice j it issues the copies of W slice j+1 and then of A slice j+2 (their
+// buffers' last readers finished in slice j-1), and at the end of the slice it
+// waits for all but the A copies just issued. A thus has two slices of lead
+// and W one. Its fragment reads are asm blocks: with five DMA targets the
+// compiler's wait insertion would otherwise make every LDS read wait for all
+// copies in flight.
+// ---------------------------------------------------------------------------
+template <int G, int SM, int SN>
+__device__ __forceinline__ void ring_slice(f32x16 (&acc)[SM][SN], bf16x8 (&fa)[2][SM], bf16x8 (&fb)[2][SN],
+                                           const bf16_t* ca, const bf16_t* cb, bf16_t* na, bf16_t* nb, int a_row0,
+                                           int b_row0, int sw, int fk, const BigCopy& cp, int j, int nk,
+                                           bool first) {
+  const bool live_w = j + 1 < nk, live_a = j + 2 < nk;
+  const uint32_t kb_w = (uint32_t)(j + 1) * GEMM_BK * 2, kb_a = (uint32_t)(j + 2) * GEMM_BK * 2;
+  // phase 0
+  if (G == 0) {
+    if (live_w) cp.slice_w(kb_w, nb);
+    if (live_a) cp.slice_a(kb_a, na);
+    read_half_wait<SM, SN>(ca, cb, a_row0, b_row0, sw, fk, 0, fa, fb);
+  } else if (!first) {
+    compute_half<SM, SN>(acc, fa, fb);
+  }
+  AENC_BARRIER();
+  // phase 1
+  if (G == 0) {
+    compute_half<SM, SN>(acc, fa, fb);
+  } else {
+    if (live_w) cp.slice_w(kb_w, nb);
+    if (live_a) cp.slice_a(kb_a, na);
+    read_half_wait<SM, SN>(ca, cb, a_row0, b_row0, sw, fk, 0, fa, fb);
+  }
+  AENC_BARRIER();
+  // phase 2
+  if (G == 0) {
+    read_half_wait<SM, SN>(ca, cb, a_row0, b_row0, sw, fk, 1, fa, fb);
+  } else {
+    compute_half<SM, SN>(acc, fa, fb);
+  }
+  AENC_BARRIER();
+  // phase 3
+  if (G == 0) {
+    compute_half<SM, SN>(acc, fa, fb);
+  } else {
+    read_half_wait<SM, SN>(ca, cb, a_row0, b_row0, sw, fk, 1, fa, fb);
+  }
+  if (live_a) wait_copies_but4();   // A slice j+1 and W slice j+1 have landed
+  else wait_copies();
+  AENC_BARRIER();
+}
+
+// Slice j sits in A buffer j mod 3 and W buffer j mod 2: six slices per trip.
+template <int G, int SM, int SN>
+__device__ __forceinline__ void ring_loop(f32x16 (&acc)[SM][SN], bf16_t* a0, bf16_t* a1, bf16_t* a2, bf16_t* w0,
+                                          bf16_t* w1, int a_row0, int b_row0, int sw, int fk, const BigCopy& cp,
+                                          int nk) {
+  bf16x8 fa[2][SM], fb[2][SN];
+#define AENC_RING_SLICE(T, CA, CB, NA, NB) \
+  if (j + T < nk)                          \
+    ring_slice<G, SM, SN>(acc, fa, fb, CA, CB, NA, NB, a_row0, b_row0, sw, fk, cp, j + T, nk, T == 0 && j == 0);
+  for (int j = 0; j < nk; j += 6) {
+    AENC_RING_SLICE(0, a0, w0, a2, w1)
+    AENC_RING_SLICE(1, a1, w1, a0, w0)
+    AENC_RING_SLICE(2, a2, w0, a1, w1)
+    AENC_RING_SLICE(3, a0, w1, a2, w0)
+    AENC_RING_SLICE(4, a1, w0, a0, w1)
+    AENC_RING_SLICE(5, a2, w1, a1, w0)
+  }
+#undef AENC_RING_SLICE
+  if (G == 1) compute_half<SM, SN>(acc, fa, fb);   // group 1's last half slice
+  AENC_BARRIER();
+}
+
+template <int EPI>
+__global__ __launch_bounds__(BIG_THREADS) void gemm_bf16_256_ring_kernel(GemmArgs g) {
+  constexpr int BM = 256, BN = 256, WM = 64, WN = 128;
+  constexpr int SM = WM / 32, SN = WN / 32;
+  __shared__ __attribute__((aligned(16))) bf16_t la0[BM * GEMM_BK];
+  __shared__ __attribute__((aligned(16))) bf16_t la1[BM * GEMM_BK];
+  __shared__ __attribute__((aligned(16))) bf16_t la2[BM * GEMM_BK];
+  __shared__ __attribute__((aligned(16))) bf16_t lw0[BN * GEMM_BK];
+  __shared__ __attribute__((aligned(16))) bf16_t lw1[BN * GEMM_BK];
+
+  int tm, tn;
+  if (!tile_of_block(g, tm, tn)) return;
+  const int M = g.m_dev ? *g.m_dev : g.M;
+  const int m0 = tm * BM, n0 = tn * BN;
+  if (m0 >= M) return;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  BigCopy cp;
+  cp.ra = make_rsrc(g.A, g.a_bytes);
+  cp.rw = make_rsrc(g.W, g.w_bytes);
+  cp.pa = plan_a<4>(g, m0, M, wave, lane);
+  cp.pw = plan_w<4>(g, n0, wave, lane);
+  cp.wave = wave;
+
+  f32x16 acc[SM][SN];
+#pragma unroll
+  for (int i = 0; i < SM; ++i)
+#pragma unroll
+    for (int j = 0; j < SN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  const int fr = lane & 31, fk = lane >> 5;
+  const int a_row0 = wm * WM + fr;
+  const int b_row0 = wn * WN + fr;
+  const int sw = (fr >> 1) & 7;
+  const int nk = g.K / GEMM_BK;
+
+  // A slices 0 and 1 and W slice 0 in flight; wait for A 0 and W 0
+  cp.slice(0, la0, lw0);
+  if (nk > 1) {
+    cp.slice_a(GEMM_BK * 2, la1);
+    wait_copies_but4();
+  } else {
+    wait_copies();
+  }
+  AENC_BARRIER();
+  if (wave < 4)
+    ring_loop<0, SM, SN>(acc, la0, la1, la2, lw0, lw1, a_row0, b_row0, sw, fk, cp, nk);
+  else
+    ring_loop<1, SM, SN>(acc, la0, la1, la2, lw0, lw1, a_row0, b_row0, sw, fk, cp, nk);
+
+  constexpr int SW = 64;   // two waves' slabs (2 x 9 KiB) per 32 KiB buffer
+  float* slab = (float*)(wave < 2 ? la0 : wave < 4 ? la1 : wave < 6 ? la2 : lw0) + (wave & 1) * (32 * (SW + 8));
+  store_tile<EPI, SM, SN, SW>(g, acc, slab, m0 + wm * WM, n0 + wn * WN, lane, M);
+}
+
+// ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
+// Long K, narrow N (the FFN's second product, 1280 x 5120 in Whisper-large):
+// the three-A-buffer kernel measured 1-4% faster there and 1-8% slower on the
+// wide products (K 1280, N 3840 or 5120), so only these shapes take it.
+static bool gemm_deep_a(int N, int K) { return K >= 4096 && N <= 2048; }
+
 template <int EPI>
 static hipError_t launch_epi(GemmArgs g, int tile_cfg, hipStream_t stream) {
   const int bt = tile_cfg == GEMM_TILE_256x256 ? 256 : 128;
@@ -486,7 +685,9 @@ static hipError_t launch_epi(GemmArgs g, int tile_cfg, hipStream_t stream) {
   g.tiles_n = (g.N + bt - 1) / bt;
   const int total = g.tiles_m * g.tiles_n;
   g.grid = (total + N_XCD - 1) / N_XCD * N_XCD;
-  if (tile_cfg == GEMM_TILE_256x256)
+  if (tile_cfg == GEMM_TILE_256x256 && gemm_deep_a(g.N, g.K))
+    hipLaunchKernelGGL((gemm_bf16_256_ring_kernel<EPI>), dim3(g.grid), dim3(BIG_THREADS), 0, stream, g);
+  else if (tile_cfg == GEMM_TILE_256x256)
     hipLaunchKernelGGL((gemm_bf16_256_kernel<EPI>), dim3(g.grid), dim3(BIG_THREADS), 0, stream, g);
   else
     hipLaunchKernelGGL((gemm_bf16_128_kernel<EPI>), dim3(g.grid), dim3(SMALL_THREADS), 0, stream, g);

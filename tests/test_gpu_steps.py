@@ -53,6 +53,7 @@ GEMM_SHAPES = [
     (1, 200, 128),
     (3000, 5120, 1280),   # FC1 of a Whisper-large clip
     (3000, 1280, 5120),   # FC2
+    (777, 1284, 4160),    # long K, narrow N, ragged M and N, 65 slices (deep-A kernel on 256x256)
 ]
 
 
