@@ -97,12 +97,18 @@ __device__ __forceinline__ void read_frags(const bf16_t* base, int row0, int ch,
   for (int i = 0; i < S; ++i) f[i] = *(const bf16x8*)(base + (row0 + 32 * i) * GEMM_BK + ch * 8);
 }
 
+// The MFMA computes the 32x32 block transposed: W rows are its first operand
+// (the rows of its result) and A rows its second. A lane then holds one row
+// of C (A row lane & 31) and 16 entries of W rows 8*(v/4) + 4*(lane>>5) +
+// v%4; the copies place W rows in LDS permuted within each 32-row block (see
+// plan_w) so that those are the 16 consecutive columns 16*(lane>>5) + v:
+//   acc[i][j][v] = C[row0 + 32 i + (lane & 31)][col0 + 32 j + 16 (lane >> 5) + v].
 template <int SM, int SN>
 __device__ __forceinline__ void mma(f32x16 (&acc)[SM][SN], const bf16x8 (&fa)[SM], const bf16x8 (&fb)[SN]) {
 #pragma unroll
   for (int i = 0; i < SM; ++i)
 #pragma unroll
-    for (int j = 0; j < SN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    for (int j = 0; j < SN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
 }
 
 // Tile (tm, tn) of workgroup blockIdx.x: XCD-contiguous ranges, then
@@ -144,6 +150,13 @@ __device__ __forceinline__ CopyPlan<NI> plan_a(const GemmArgs& g, int m0, int M,
   return p;
 }
 
+// W rows go to LDS permuted within each 32-row block: LDS row r = 8 g + 4 h + q
+// (g < 4, h < 2, q < 4) holds W row 16 h + 4 g + q of the block, which makes
+// the MFMA result rows a lane holds (see mma) consecutive output columns.
+__device__ __forceinline__ int w_row_of_lds_row(int r) {
+  return (r & ~31) | (((r >> 2) & 1) << 4) | (((r >> 3) & 3) << 2) | (r & 3);
+}
+
 template <int NI>
 __device__ __forceinline__ CopyPlan<NI> plan_w(const GemmArgs& g, int n0, int wave, int lane) {
   const int c_row = lane >> 3;
@@ -152,30 +165,93 @@ __device__ __forceinline__ CopyPlan<NI> plan_w(const GemmArgs& g, int n0, int wa
   for (int i = 0; i < NI; ++i) {
     const int row0 = (wave * NI + i) * 8;
     const int ch = (lane & 7) ^ ((c_row >> 1) + ((row0 & 8) ? 4 : 0));
-    p.off[i] = (uint32_t)(((int64_t)min(n0 + row0 + c_row, g.N - 1) * g.ldw + ch * 8) * 2);
+    const int n = n0 + w_row_of_lds_row(row0 + c_row);
+    p.off[i] = (uint32_t)(((int64_t)min(n, g.N - 1) * g.ldw + ch * 8) * 2);
   }
   return p;
 }
 
-// Epilogue through LDS: a wave stages its fp32 accumulators as 32-row slabs
-// SW columns wide (lane holds column lane&31 and rows 8*(v/4) + 4*(lane>>5) +
-// v%4 of each 32x32 sub-tile), then writes each slab back row-contiguously.
-// Slab rows are padded to SW + 8 floats: lanes 32-63 write 4 rows below lanes
-// 0-31, which then lands on the other half of the 64 banks.
+// Epilogue. A lane holds 16 consecutive columns of one row per 32x32 block
+// (see mma), so bf16 outputs are finished in registers and written directly,
+// 16 bytes per lane (8 columns). fp32 outputs and the V^T part of the QKV
+// epilogue go through LDS instead: a wave stages its accumulators as 32-row
+// slabs SW columns wide (16-byte writes; rows padded to SW + 4 floats so that
+// the 16 lanes of one write cycle cover all 64 banks), then writes each slab
+// back row-contiguously (or column-contiguously for V^T). Staging measured
+// faster for the fp32 residual update (its loads and stores stay fully
+// coalesced) and slower for bf16 stores.
+template <int EPI, int SM, int SN>
+__device__ __forceinline__ void store_direct_bf16(const GemmArgs& g, const f32x16 (&acc)[SM][SN], int row0, int col0,
+                                                  int lane, int M) {
+  const EpiParams& p = g.epi;
+  const int fr = lane & 31, fk = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < SM; ++i) {
+    const int m = row0 + 32 * i + fr;
+    const int64_t o = m < M ? p.crow.offset(m) : -1;
+    if (o < 0) continue;
+    bf16_t* const crow = (bf16_t*)p.c + o;
+#pragma unroll
+    for (int j = 0; j < SN; ++j) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int n = col0 + 32 * j + 16 * fk + 8 * c;
+        if (n >= g.N) continue;
+        const bool full = n + 8 <= g.N;   // else 4 columns (N is a multiple of 4)
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = acc[i][j][8 * c + e];
+        if (p.bias) {
+          const float4 b0 = *(const float4*)(p.bias + n);
+          const float4 b1 = full ? *(const float4*)(p.bias + n + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+          v[0] += b0.x; v[1] += b0.y; v[2] += b0.z; v[3] += b0.w;
+          v[4] += b1.x; v[5] += b1.y; v[6] += b1.z; v[7] += b1.w;
+        }
+        if (EPI == EPI_QKV_BF16 && n < p.q_cols) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] *= p.q_scale;
+        }
+        if (EPI == EPI_GELU_BF16) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = gelu_bf16out(v[e]);
+        }
+        u32x2 lo, hi;
+        lo.x = pack_bf16x2(v[0], v[1]);
+        lo.y = pack_bf16x2(v[2], v[3]);
+        hi.x = pack_bf16x2(v[4], v[5]);
+        hi.y = pack_bf16x2(v[6], v[7]);
+        if (full && ((o + n) & 7) == 0) {
+          *(uint4*)(crow + n) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        } else {
+          *(u32x2*)(crow + n) = lo;
+          if (full) *(u32x2*)(crow + n + 4) = hi;
+        }
+      }
+    }
+  }
+}
+
 template <int EPI, int SM, int SN, int SW>
 __device__ __forceinline__ void store_tile(const GemmArgs& g, const f32x16 (&acc)[SM][SN], float* slab, int row0,
                                            int col0, int lane, int M) {
-  constexpr int LDW = SW + 8, JW = SW / 32;
+  if (EPI == EPI_STORE_BF16 || EPI == EPI_GELU_BF16 || (EPI == EPI_QKV_BF16 && col0 < g.epi.n_split)) {
+    store_direct_bf16<EPI, SM, SN>(g, acc, row0, col0, lane, M);
+    return;
+  }
+  constexpr int LDW = SW + 4, JW = SW / 32;
   const int fr = lane & 31, fk = lane >> 5;
 #pragma unroll
   for (int i = 0; i < SM; ++i) {
 #pragma unroll
     for (int jh = 0; jh < SN / JW; ++jh) {
 #pragma unroll
-      for (int j = 0; j < JW; ++j)
+      for (int j = 0; j < JW; ++j) {
+        const f32x16& a = acc[i][jh * JW + j];
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-          slab[(8 * (v >> 2) + 4 * fk + (v & 3)) * LDW + 32 * j + fr] = acc[i][jh * JW + j][v];
+        for (int q = 0; q < 4; ++q)
+          *(float4*)(slab + fr * LDW + 32 * j + 16 * fk + 4 * q) =
+              make_float4(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
+      }
       wait_lds();   // the slab is written
       __builtin_amdgcn_wave_barrier();
       Epilogue<EPI>::template slab32<SW, LDW>(g.epi, slab, row0 + 32 * i, col0 + SW * jh, lane, M, g.N);
@@ -319,7 +395,7 @@ __global__ __launch_bounds__(SMALL_THREADS) void gemm_bf16_128_kernel(GemmArgs g
   }
 
   constexpr int SW = WN;
-  float* slab = (float*)(wave < 2 ? buf0 : buf1) + (wave & 1) * (32 * (SW + 8));
+  float* slab = (float*)(wave < 2 ? buf0 : buf1) + (wave & 1) * (32 * (SW + 4));
   store_tile<EPI, SM, SN, SW>(g, acc, slab, m0 + wm * WM, n0 + wn * WN, lane, M);
 }
 
@@ -532,7 +608,7 @@ __global__ __launch_bounds__(BIG_THREADS) void gemm_bf16_256_kernel(GemmArgs g) 
     big_loop<1, SM, SN>(acc, a0, b0, a1, b1, a_row0, b_row0, sw, fk, cp, nk);
 
   constexpr int SW = 64;
-  float* slab = (float*)(wave < 4 ? buf0 : buf1) + (wave & 3) * (32 * (SW + 8));
+  float* slab = (float*)(wave < 4 ? buf0 : buf1) + (wave & 3) * (32 * (SW + 4));
   store_tile<EPI, SM, SN, SW>(g, acc, slab, m0 + wm * WM, n0 + wn * WN, lane, M);
 }
 
@@ -665,8 +741,8 @@ __global__ __launch_bounds__(BIG_THREADS) void gemm_bf16_256_ring_kernel(GemmArg
   else
     ring_loop<1, SM, SN>(acc, la0, la1, la2, lw0, lw1, a_row0, b_row0, sw, fk, cp, nk);
 
-  constexpr int SW = 64;   // two waves' slabs (2 x 9 KiB) per 32 KiB buffer
-  float* slab = (float*)(wave < 2 ? la0 : wave < 4 ? la1 : wave < 6 ? la2 : lw0) + (wave & 1) * (32 * (SW + 8));
+  constexpr int SW = 64;   // two waves' slabs (2 x 8.5 KiB) per 32 KiB buffer
+  float* slab = (float*)(wave < 2 ? la0 : wave < 4 ? la1 : wave < 6 ? la2 : lw0) + (wave & 1) * (32 * (SW + 4));
   store_tile<EPI, SM, SN, SW>(g, acc, slab, m0 + wm * WM, n0 + wn * WN, lane, M);
 }
 
