@@ -173,8 +173,11 @@ __global__ __launch_bounds__(256) void attention_bf16_kernel(const bf16_t* __res
 
   // One 64-key tile from LDS buffer `buf`; MASKED: keys past the clip (or, RANGED,
   // outside the query's range) are masked.
-  auto tile = [&](int buf, int k0, auto masked) {
+  auto tile = [&](int buf, int k0, auto masked, auto first) {
     constexpr bool MASKED = decltype(masked)::value;
+    // Without ranges every row sees key 0 in the first tile, so no row can
+    // still be waiting for its first key after it.
+    constexpr bool MAYBE_FRESH = RANGED || decltype(first)::value;
     // ---- S^T - m_run = K Q^T - m_run for two 32-key sub-tiles ----
     f32x16 s[2];
 #pragma unroll
@@ -211,7 +214,7 @@ __global__ __launch_bounds__(256) void attention_bf16_kernel(const bf16_t* __res
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));                  // the row's tile maximum, relative to m_run
     // Move the reference when some row outgrew it by more than the slack, or
     // sees its first key (a uniform branch, rarely taken after the first tile).
-    const bool fresh = m_run == -INFINITY;
+    const bool fresh = MAYBE_FRESH && m_run == -INFINITY;
     if (__any(fresh ? mx > -INFINITY : mx > slack)) {
       const float shift = fresh ? (mx == -INFINITY ? 0.0f : mx) : fmaxf(mx, 0.0f);
       const float alpha = fresh ? 1.0f : __builtin_amdgcn_exp2f(-shift);
@@ -266,16 +269,19 @@ __global__ __launch_bounds__(256) void attention_bf16_kernel(const bf16_t* __res
   else gload(kt_first * ATT_BK, std::false_type{});
   lstore(0);
   __syncthreads();
-  for (int kt = kt_first; kt < kt_last; ++kt) {
-    const int buf = (kt - kt_first) & 1;
+  // full tile kt from buffer buf, with the next one loaded meanwhile
+  auto step = [&](int kt, int buf, auto first) {
     if ((kt + 2) * ATT_BK > len) gload((kt + 1) * ATT_BK, std::true_type{});
     else gload((kt + 1) * ATT_BK, std::false_type{});
-    if (RANGED) tile(buf, kt * ATT_BK, std::true_type{});
-    else tile(buf, kt * ATT_BK, std::false_type{});
+    tile(buf, kt * ATT_BK, std::integral_constant<bool, RANGED>{}, first);
     lstore(buf ^ 1);
     __syncthreads();
-  }
-  tile((kt_last - kt_first) & 1, kt_last * ATT_BK, std::true_type{});
+  };
+  if (kt_first < kt_last) step(kt_first, 0, std::true_type{});
+  for (int kt = kt_first + 1; kt < kt_last; ++kt) step(kt, (kt - kt_first) & 1, std::false_type{});
+  // the last tile (masked); it is also the first when the workgroup visits one tile
+  if (kt_last == kt_first) tile(0, kt_last * ATT_BK, std::true_type{}, std::true_type{});
+  else tile((kt_last - kt_first) & 1, kt_last * ATT_BK, std::true_type{}, std::false_type{});
 
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = 1.0f / l_tot;
