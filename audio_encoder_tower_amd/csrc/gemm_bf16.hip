@@ -5,13 +5,13 @@
 // is row-major (the [out, in] checkpoint layout). K must be a multiple of 64.
 // Every wave issues v_mfma_f32_32x32x16_bf16 on 32x32 sub-tiles of C.
 //
-// K advances in slices of 64 through two LDS buffers. Slices are copied
+// K advances in slices of 64 through LDS buffers. Slices are copied
 // global -> LDS by buffer_load_dwordx4 ... lds (direct to LDS, gfx950): no
 // staging registers and no LDS write instructions, and the slice's K offset
 // rides in the scalar offset, so a copy instruction needs no per-lane address
 // arithmetic. The buffers are distinct LDS objects and the slice loop is
-// unrolled by two, so the copy into one buffer never forces a wait in front
-// of the reads of the other.
+// unrolled over them, so a copy into one buffer never forces a wait in front
+// of the reads of another.
 //
 // LDS rows are 128 bytes (64 bf16 of K). The LDS serves a 128-bit read for 16
 // lanes per cycle from 64 four-byte banks, i.e. two rows' worth of banks, so
@@ -26,10 +26,10 @@
 //    groups that alternate roles every phase (ping-pong): while one group's
 //    waves run a burst of 16 MFMAs at raised priority, the other group's
 //    waves, on the same SIMDs, read their next fragments from LDS and issue
-//    the copies of the next slice; a workgroup barrier ends each phase. One
-//    workgroup per CU (128 KiB of LDS). Used for the large GEMMs. A variant
-//    for long K and narrow N gives A three LDS buffers (160 KiB in all), so
-//    A slices are requested two slices ahead.
+//    copies of coming slices; a workgroup barrier ends each phase. Three A
+//    and two W slice buffers fill the CU's 160 KiB of LDS (one workgroup per
+//    CU), so A slices are requested two slices ahead. Used for the large
+//    GEMMs.
 //  * 128x128, 4 waves, each wave 64x64, two workgroups per CU that overlap
 //    each other's copies and MFMAs. Used when the 256x256 tiles would leave
 //    most CUs idle (short batches).
@@ -404,22 +404,12 @@ __global__ __launch_bounds__(SMALL_THREADS) void gemm_bf16_128_kernel(GemmArgs g
 // ---------------------------------------------------------------------------
 constexpr int BIG_THREADS = 512;
 
-// Fragments of half a slice (two K steps).
-template <int SM, int SN>
-__device__ __forceinline__ void read_half(const bf16_t* as, const bf16_t* bs, int a_row0, int b_row0, int sw,
-                                          int fk, int h, bf16x8 (&fa)[2][SM], bf16x8 (&fb)[2][SN]) {
-  read_frags<SM>(as, a_row0, (4 * h + 0 + fk) ^ sw, fa[0]);
-  read_frags<SN>(bs, b_row0, (4 * h + 0 + fk) ^ sw, fb[0]);
-  read_frags<SM>(as, a_row0, (4 * h + 2 + fk) ^ sw, fa[1]);
-  read_frags<SN>(bs, b_row0, (4 * h + 2 + fk) ^ sw, fb[1]);
-}
-
 typedef int i32x4_asm __attribute__((ext_vector_type(4)));
 
-// read_half plus the wait for it, as one asm block: the compiler's wait
-// insertion then never sees these LDS reads, so it does not make them wait for
-// the direct-to-LDS copies in flight (it cannot tell that those target other
-// buffers once there are more than two).
+// The fragments of half a slice (two K steps) and the wait for them, as one
+// asm block: the compiler's wait insertion then never sees these LDS reads, so
+// it does not make them wait for the direct-to-LDS copies in flight (it cannot
+// tell that those target other buffers once there are more than two).
 template <int SM, int SN>
 __device__ __forceinline__ void read_half_wait(const bf16_t* as, const bf16_t* bs, int a_row0, int b_row0, int sw,
                                                int fk, int h, bf16x8 (&fa)[2][SM], bf16x8 (&fb)[2][SN]) {
@@ -497,134 +487,20 @@ __device__ __forceinline__ void wait_copies_but4() { __builtin_amdgcn_s_waitcnt(
 // One K slice in four phases, each closed by a workgroup barrier. Group 0
 // reads fragments (half 0, then half 1) in phases 0 and 2 and multiplies in
 // 1 and 3; group 1 runs one phase later (its phase-0 work is the second half
-// of the previous slice). Both groups copy the next slice into the other
-// buffer as they start reading this one (its last readers finished in the
-// previous slice's phase 3) and wait for their copies at the end of phase 3.
+// of the previous slice). A slices run through three LDS buffers and W slices
+// through two (160 KiB in all). As each group reads the first half of slice
+// j it copies W slice j+1, and as it reads the second half, A slice j+2 (the
+// buffers' last readers finished in slice j-1); at the end of the slice it
+// waits for all but the A copies just issued. A (the activations, streamed
+// from memory) thus has about one and a half slices of lead and W (shared by
+// many tiles, mostly L2 hits) about one, and the copy path carries a quarter
+// slice per phase: issuing a whole slice in one phase (two of four phases
+// with copies) saturated the ~64 B/clk per CU of direct-to-LDS copies and
+// left the phases without copies idle (fc2 6% slower). The fragment reads are
+// asm blocks: with five DMA targets the compiler's wait insertion would
+// otherwise make every LDS read wait for all copies in flight.
 template <int G, int SM, int SN>
 __device__ __forceinline__ void big_slice(f32x16 (&acc)[SM][SN], bf16x8 (&fa)[2][SM], bf16x8 (&fb)[2][SN],
-                                          const bf16_t* ca, const bf16_t* cb, bf16_t* na, bf16_t* nb, int a_row0,
-                                          int b_row0, int sw, int fk, const BigCopy& cp, uint32_t k_next,
-                                          bool live, bool first) {
-  // phase 0
-  if (G == 0) {
-    if (live) cp.slice(k_next, na, nb);
-    read_half<SM, SN>(ca, cb, a_row0, b_row0, sw, fk, 0, fa, fb);
-    wait_lds();
-  } else if (!first) {
-    compute_half<SM, SN>(acc, fa, fb);
-  }
-  AENC_BARRIER();
-  // phase 1
-  if (G == 0) {
-    compute_half<SM, SN>(acc, fa, fb);
-  } else {
-    if (live) cp.slice(k_next, na, nb);
-    read_half<SM, SN>(ca, cb, a_row0, b_row0, sw, fk, 0, fa, fb);
-    wait_lds();
-  }
-  AENC_BARRIER();
-  // phase 2
-  if (G == 0) {
-    read_half<SM, SN>(ca, cb, a_row0, b_row0, sw, fk, 1, fa, fb);
-    wait_lds();
-  } else {
-    compute_half<SM, SN>(acc, fa, fb);
-  }
-  AENC_BARRIER();
-  // phase 3
-  if (G == 0) {
-    compute_half<SM, SN>(acc, fa, fb);
-  } else {
-    read_half<SM, SN>(ca, cb, a_row0, b_row0, sw, fk, 1, fa, fb);
-    wait_lds();
-  }
-  wait_copies();
-  AENC_BARRIER();
-}
-
-template <int G, int SM, int SN>
-__device__ __forceinline__ void big_loop(f32x16 (&acc)[SM][SN], bf16_t* a0, bf16_t* b0, bf16_t* a1, bf16_t* b1,
-                                         int a_row0, int b_row0, int sw, int fk, const BigCopy& cp, int nk) {
-  bf16x8 fa[2][SM], fb[2][SN];
-  int kt = 0;
-  for (; kt + 1 < nk; kt += 2) {
-    big_slice<G, SM, SN>(acc, fa, fb, a0, b0, a1, b1, a_row0, b_row0, sw, fk, cp, (uint32_t)(kt + 1) * GEMM_BK * 2,
-                         true, kt == 0);
-    big_slice<G, SM, SN>(acc, fa, fb, a1, b1, a0, b0, a_row0, b_row0, sw, fk, cp, (uint32_t)(kt + 2) * GEMM_BK * 2,
-                         kt + 2 < nk, false);
-  }
-  if (kt < nk)   // odd slice count: the last slice sits in buffer 0
-    big_slice<G, SM, SN>(acc, fa, fb, a0, b0, a1, b1, a_row0, b_row0, sw, fk, cp, 0, false, kt == 0);
-  if (G == 1) compute_half<SM, SN>(acc, fa, fb);   // group 1's last half slice
-  AENC_BARRIER();
-}
-
-template <int EPI>
-__global__ __launch_bounds__(BIG_THREADS) void gemm_bf16_256_kernel(GemmArgs g) {
-  constexpr int BM = 256, BN = 256, WM = 64, WN = 128;
-  constexpr int SM = WM / 32, SN = WN / 32;
-  __shared__ __attribute__((aligned(16))) bf16_t buf0[(BM + BN) * GEMM_BK];
-  __shared__ __attribute__((aligned(16))) bf16_t buf1[(BM + BN) * GEMM_BK];
-
-  int tm, tn;
-  if (!tile_of_block(g, tm, tn)) return;
-  const int M = g.m_dev ? *g.m_dev : g.M;
-  const int m0 = tm * BM, n0 = tn * BN;
-  if (m0 >= M) return;
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  BigCopy cp;
-  cp.ra = make_rsrc(g.A, g.a_bytes);
-  cp.rw = make_rsrc(g.W, g.w_bytes);
-  cp.pa = plan_a<4>(g, m0, M, wave, lane);
-  cp.pw = plan_w<4>(g, n0, wave, lane);
-  cp.wave = wave;
-
-  f32x16 acc[SM][SN];
-#pragma unroll
-  for (int i = 0; i < SM; ++i)
-#pragma unroll
-    for (int j = 0; j < SN; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-
-  const int fr = lane & 31, fk = lane >> 5;
-  const int a_row0 = wm * WM + fr;
-  const int b_row0 = wn * WN + fr;
-  const int sw = (fr >> 1) & 7;
-  bf16_t* const a0 = buf0;
-  bf16_t* const b0 = buf0 + BM * GEMM_BK;
-  bf16_t* const a1 = buf1;
-  bf16_t* const b1 = buf1 + BM * GEMM_BK;
-  const int nk = g.K / GEMM_BK;
-
-  cp.slice(0, a0, b0);
-  wait_copies();
-  AENC_BARRIER();
-  if (wave < 4)
-    big_loop<0, SM, SN>(acc, a0, b0, a1, b1, a_row0, b_row0, sw, fk, cp, nk);
-  else
-    big_loop<1, SM, SN>(acc, a0, b0, a1, b1, a_row0, b_row0, sw, fk, cp, nk);
-
-  constexpr int SW = 64;
-  float* slab = (float*)(wave < 4 ? buf0 : buf1) + (wave & 3) * (32 * (SW + 4));
-  store_tile<EPI, SM, SN, SW>(g, acc, slab, m0 + wm * WM, n0 + wn * WN, lane, M);
-}
-
-// ---------------------------------------------------------------------------
-// 256x256 tiles with a deeper A prefetch, for long K and narrow N (the FFN's
-// second product). The same 8-wave ping-pong, but A slices run through three
-// LDS buffers and W slices through two (160 KiB): as each group starts reading
-// slice j it issues the copies of W slice j+1 and then of A slice j+2 (their
-// buffers' last readers finished in slice j-1), and at the end of the slice it
-// waits for all but the A copies just issued. A thus has two slices of lead
-// and W one. Its fragment reads are asm blocks: with five DMA targets the
-// compiler's wait insertion would otherwise make every LDS read wait for all
-// copies in flight.
-// ---------------------------------------------------------------------------
-template <int G, int SM, int SN>
-__device__ __forceinline__ void ring_slice(f32x16 (&acc)[SM][SN], bf16x8 (&fa)[2][SM], bf16x8 (&fb)[2][SN],
                                            const bf16_t* ca, const bf16_t* cb, bf16_t* na, bf16_t* nb, int a_row0,
                                            int b_row0, int sw, int fk, const BigCopy& cp, int j, int nk,
                                            bool first) {
@@ -633,7 +509,6 @@ __device__ __forceinline__ void ring_slice(f32x16 (&acc)[SM][SN], bf16x8 (&fa)[2
   // phase 0
   if (G == 0) {
     if (live_w) cp.slice_w(kb_w, nb);
-    if (live_a) cp.slice_a(kb_a, na);
     read_half_wait<SM, SN>(ca, cb, a_row0, b_row0, sw, fk, 0, fa, fb);
   } else if (!first) {
     compute_half<SM, SN>(acc, fa, fb);
@@ -644,12 +519,12 @@ __device__ __forceinline__ void ring_slice(f32x16 (&acc)[SM][SN], bf16x8 (&fa)[2
     compute_half<SM, SN>(acc, fa, fb);
   } else {
     if (live_w) cp.slice_w(kb_w, nb);
-    if (live_a) cp.slice_a(kb_a, na);
     read_half_wait<SM, SN>(ca, cb, a_row0, b_row0, sw, fk, 0, fa, fb);
   }
   AENC_BARRIER();
   // phase 2
   if (G == 0) {
+    if (live_a) cp.slice_a(kb_a, na);
     read_half_wait<SM, SN>(ca, cb, a_row0, b_row0, sw, fk, 1, fa, fb);
   } else {
     compute_half<SM, SN>(acc, fa, fb);
@@ -659,6 +534,7 @@ __device__ __forceinline__ void ring_slice(f32x16 (&acc)[SM][SN], bf16x8 (&fa)[2
   if (G == 0) {
     compute_half<SM, SN>(acc, fa, fb);
   } else {
+    if (live_a) cp.slice_a(kb_a, na);
     read_half_wait<SM, SN>(ca, cb, a_row0, b_row0, sw, fk, 1, fa, fb);
   }
   if (live_a) wait_copies_but4();   // A slice j+1 and W slice j+1 have landed
@@ -668,28 +544,28 @@ __device__ __forceinline__ void ring_slice(f32x16 (&acc)[SM][SN], bf16x8 (&fa)[2
 
 // Slice j sits in A buffer j mod 3 and W buffer j mod 2: six slices per trip.
 template <int G, int SM, int SN>
-__device__ __forceinline__ void ring_loop(f32x16 (&acc)[SM][SN], bf16_t* a0, bf16_t* a1, bf16_t* a2, bf16_t* w0,
+__device__ __forceinline__ void big_loop(f32x16 (&acc)[SM][SN], bf16_t* a0, bf16_t* a1, bf16_t* a2, bf16_t* w0,
                                           bf16_t* w1, int a_row0, int b_row0, int sw, int fk, const BigCopy& cp,
                                           int nk) {
   bf16x8 fa[2][SM], fb[2][SN];
-#define AENC_RING_SLICE(T, CA, CB, NA, NB) \
+#define AENC_BIG_SLICE(T, CA, CB, NA, NB) \
   if (j + T < nk)                          \
-    ring_slice<G, SM, SN>(acc, fa, fb, CA, CB, NA, NB, a_row0, b_row0, sw, fk, cp, j + T, nk, T == 0 && j == 0);
+    big_slice<G, SM, SN>(acc, fa, fb, CA, CB, NA, NB, a_row0, b_row0, sw, fk, cp, j + T, nk, T == 0 && j == 0);
   for (int j = 0; j < nk; j += 6) {
-    AENC_RING_SLICE(0, a0, w0, a2, w1)
-    AENC_RING_SLICE(1, a1, w1, a0, w0)
-    AENC_RING_SLICE(2, a2, w0, a1, w1)
-    AENC_RING_SLICE(3, a0, w1, a2, w0)
-    AENC_RING_SLICE(4, a1, w0, a0, w1)
-    AENC_RING_SLICE(5, a2, w1, a1, w0)
+    AENC_BIG_SLICE(0, a0, w0, a2, w1)
+    AENC_BIG_SLICE(1, a1, w1, a0, w0)
+    AENC_BIG_SLICE(2, a2, w0, a1, w1)
+    AENC_BIG_SLICE(3, a0, w1, a2, w0)
+    AENC_BIG_SLICE(4, a1, w0, a0, w1)
+    AENC_BIG_SLICE(5, a2, w1, a1, w0)
   }
-#undef AENC_RING_SLICE
+#undef AENC_BIG_SLICE
   if (G == 1) compute_half<SM, SN>(acc, fa, fb);   // group 1's last half slice
   AENC_BARRIER();
 }
 
 template <int EPI>
-__global__ __launch_bounds__(BIG_THREADS) void gemm_bf16_256_ring_kernel(GemmArgs g) {
+__global__ __launch_bounds__(BIG_THREADS) void gemm_bf16_256_kernel(GemmArgs g) {
   constexpr int BM = 256, BN = 256, WM = 64, WN = 128;
   constexpr int SM = WM / 32, SN = WN / 32;
   __shared__ __attribute__((aligned(16))) bf16_t la0[BM * GEMM_BK];
@@ -737,9 +613,9 @@ __global__ __launch_bounds__(BIG_THREADS) void gemm_bf16_256_ring_kernel(GemmArg
   }
   AENC_BARRIER();
   if (wave < 4)
-    ring_loop<0, SM, SN>(acc, la0, la1, la2, lw0, lw1, a_row0, b_row0, sw, fk, cp, nk);
+    big_loop<0, SM, SN>(acc, la0, la1, la2, lw0, lw1, a_row0, b_row0, sw, fk, cp, nk);
   else
-    ring_loop<1, SM, SN>(acc, la0, la1, la2, lw0, lw1, a_row0, b_row0, sw, fk, cp, nk);
+    big_loop<1, SM, SN>(acc, la0, la1, la2, lw0, lw1, a_row0, b_row0, sw, fk, cp, nk);
 
   constexpr int SW = 64;   // two waves' slabs (2 x 8.5 KiB) per 32 KiB buffer
   float* slab = (float*)(wave < 2 ? la0 : wave < 4 ? la1 : wave < 6 ? la2 : lw0) + (wave & 1) * (32 * (SW + 4));
@@ -749,11 +625,6 @@ __global__ __launch_bounds__(BIG_THREADS) void gemm_bf16_256_ring_kernel(GemmArg
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
-// Long K, narrow N (the FFN's second product, 1280 x 5120 in Whisper-large):
-// the three-A-buffer kernel measured 1-4% faster there and 1-8% slower on the
-// wide products (K 1280, N 3840 or 5120), so only these shapes take it.
-static bool gemm_deep_a(int N, int K) { return K >= 4096 && N <= 2048; }
-
 template <int EPI>
 static hipError_t launch_epi(GemmArgs g, int tile_cfg, hipStream_t stream) {
   const int bt = tile_cfg == GEMM_TILE_256x256 ? 256 : 128;
@@ -761,9 +632,7 @@ static hipError_t launch_epi(GemmArgs g, int tile_cfg, hipStream_t stream) {
   g.tiles_n = (g.N + bt - 1) / bt;
   const int total = g.tiles_m * g.tiles_n;
   g.grid = (total + N_XCD - 1) / N_XCD * N_XCD;
-  if (tile_cfg == GEMM_TILE_256x256 && gemm_deep_a(g.N, g.K))
-    hipLaunchKernelGGL((gemm_bf16_256_ring_kernel<EPI>), dim3(g.grid), dim3(BIG_THREADS), 0, stream, g);
-  else if (tile_cfg == GEMM_TILE_256x256)
+  if (tile_cfg == GEMM_TILE_256x256)
     hipLaunchKernelGGL((gemm_bf16_256_kernel<EPI>), dim3(g.grid), dim3(BIG_THREADS), 0, stream, g);
   else
     hipLaunchKernelGGL((gemm_bf16_128_kernel<EPI>), dim3(g.grid), dim3(SMALL_THREADS), 0, stream, g);

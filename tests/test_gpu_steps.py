@@ -53,7 +53,7 @@ GEMM_SHAPES = [
     (1, 200, 128),
     (3000, 5120, 1280),   # FC1 of a Whisper-large clip
     (3000, 1280, 5120),   # FC2
-    (777, 1284, 4160),    # long K, narrow N, ragged M and N, 65 slices (deep-A kernel on 256x256)
+    (777, 1284, 4160),    # ragged M and N, 65 slices: a partial trip of the 6-slice buffer cycle
     (70, 196, 64),        # N = 4 mod 8: 4-column tails and rows not 16-byte aligned
 ]
 
