@@ -26,6 +26,9 @@ int hip_status(hipError_t e, const char* what) {
   aenc::set_kernel_error(buf);
   return AENC_E_HIP;
 }
+// The kernels move 16 bytes per lane (direct-to-LDS copies, fragment loads,
+// row stores), so operand base addresses must be 16-byte aligned.
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 }  // namespace
 
 extern "C" int aenc_k_gemm_bf16(int epi, const void* A, int64_t lda, const void* W, const float* bias, void* C,
@@ -33,6 +36,8 @@ extern "C" int aenc_k_gemm_bf16(int epi, const void* A, int64_t lda, const void*
   if (!A || !W || !C) return fail("NULL operand");
   if (M < 1 || N < 1 || N % 4 || K < 64 || K % 64 || lda < K || lda % 8 || ldc < N || ldc % 4)
     return fail("bad GEMM sizes (need N % 4 == 0, K % 64 == 0, lda % 8 == 0, ldc % 4 == 0)");
+  if (!aligned16(A) || !aligned16(W) || !aligned16(C) || !aligned16(bias))
+    return fail("GEMM operands must be 16-byte aligned");
   int kind;
   switch (epi) {
     case AENC_EPI_BF16: kind = EPI_STORE_BF16; break;
@@ -55,6 +60,8 @@ extern "C" int aenc_k_qkv_bf16(const void* A, const void* Wqkv, const float* bia
                                void* vt, int64_t ld_vt, int M, int d, void* stream) {
   if (!A || !Wqkv || !qk || !vt) return fail("NULL operand");
   if (M < 1 || d < 64 || d % 64 || ld_vt < M + 64 || ld_vt % 8) return fail("bad QKV sizes");
+  if (!aligned16(A) || !aligned16(Wqkv) || !aligned16(bias) || !aligned16(qk) || !aligned16(vt))
+    return fail("QKV operands must be 16-byte aligned");
   if (!(q_scale > 0.0f) || !std::isfinite(q_scale)) return fail("q_scale must be positive and finite");
   EpiParams ep{};
   ep.q_cols = q_scale == 1.0f ? 0 : d;
@@ -75,6 +82,7 @@ extern "C" int aenc_k_attention_bf16(const void* qk, const void* vt, int64_t ld_
   if (!qk || !vt || !start || !len || !out) return fail("NULL operand");
   if (!key_lo != !key_hi) return fail("key_lo and key_hi go together");
   if (n_clips < 1 || max_len < 1 || n_heads < 1 || ld_vt % 8) return fail("bad attention sizes");
+  if (!aligned16(qk) || !aligned16(vt) || !aligned16(out)) return fail("attention operands must be 16-byte aligned");
   const int d = 64 * n_heads;
   return hip_status(attention_bf16((const bf16_t*)qk, 2 * d, (const bf16_t*)vt, ld_vt, start, len, n_clips, max_len,
                                    n_heads, (bf16_t*)out, d, key_lo, key_hi, (hipStream_t)stream), "attention");

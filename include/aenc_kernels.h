@@ -37,8 +37,9 @@ enum { AENC_TILE_256x256 = 0, AENC_TILE_128x128 = 1 };
 
 /* C[M, N] = epi(A[M, K] W[N, K]^T + bias[N]) with bf16 A and W (row-major,
  * leading dimensions lda, K and ldc in elements), fp32 accumulate.
- * bias: fp32 [N] or NULL, 16-byte aligned. K must be a positive multiple of
- * 64; N a positive multiple of 4; lda a multiple of 8 and ldc of 4; M >= 1. */
+ * bias: fp32 [N] or NULL. A, W, C and bias must be 16-byte aligned. K must be
+ * a positive multiple of 64; N a positive multiple of 4; lda a multiple of 8
+ * and ldc of 4; M >= 1. */
 int aenc_k_gemm_bf16(int epi, const void *A, int64_t lda, const void *W, const float *bias, void *C,
                      int64_t ldc, int M, int N, int K, int tile, void *stream);
 
@@ -51,7 +52,8 @@ int aenc_k_gemm_bf16(int epi, const void *A, int64_t lda, const void *W, const f
  * multiplied by q_scale (> 0; 1 for plain Q, AENC_ATTN_Q_SCALE for the input
  * of aenc_k_attention_bf16) before rounding. Q and K go to qk (bf16 [M, 2d]);
  * V goes transposed to vt (bf16, row e of [d, ld_vt] holds feature e of every
- * row; ld_vt >= M + 64, a multiple of 8). d = 64 * heads. */
+ * row; ld_vt >= M + 64, a multiple of 8). d = 64 * heads. A, Wqkv, bias, qk
+ * and vt must be 16-byte aligned. */
 int aenc_k_qkv_bf16(const void *A, const void *Wqkv, const float *bias, float q_scale, void *qk, void *vt,
                     int64_t ld_vt, int M, int d, void *stream);
 
@@ -64,7 +66,8 @@ int aenc_k_qkv_bf16(const void *A, const void *Wqkv, const float *bias, float q_
  * key_lo, key_hi: NULL (every query sees its whole clip) or int32 [rows]: the
  * query at packed row r sees the clip-relative keys [key_lo[r], key_hi[r]);
  * within a clip the ranges must be non-empty, inside [0, len[b]] and
- * non-decreasing in r (as aenc_k_chunk_ranges writes them); not checked. */
+ * non-decreasing in r (as aenc_k_chunk_ranges writes them); not checked.
+ * qk, vt and out must be 16-byte aligned. */
 int aenc_k_attention_bf16(const void *qk, const void *vt, int64_t ld_vt, const int32_t *start, const int32_t *len,
                           int n_clips, int max_len, int n_heads, const int32_t *key_lo, const int32_t *key_hi,
                           void *out, void *stream);

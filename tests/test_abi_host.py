@@ -145,6 +145,16 @@ def test_null_arguments(aenc):
     buf = ctypes.c_void_p(16)
     assert L.aenc_k_gemm_bf16(0, buf, 64, buf, None, buf, 64, 64, 64, 100, -1, None) == -1
     assert L.aenc_k_layernorm(buf, buf, buf, buf, 0, 4, 4096, 1e-5, None) == -1
+    # ... and operands not 16-byte aligned (the kernels move 16 bytes per lane)
+    odd = ctypes.c_void_p(24)
+    assert L.aenc_k_gemm_bf16(0, buf, 64, buf, None, odd, 64, 64, 64, 64, -1, None) == -1
+    assert "aligned" in aenc.last_error()
+    assert L.aenc_k_gemm_bf16(0, odd, 64, buf, None, buf, 64, 64, 64, 64, -1, None) == -1
+    assert L.aenc_k_qkv_bf16(buf, buf, odd, ctypes.c_float(1.0), buf, buf, 128, 64, 64, None) == -1
+    assert "aligned" in aenc.last_error()
+    i32 = ctypes.c_void_p(64)
+    assert L.aenc_k_attention_bf16(buf, buf, 64, i32, i32, 1, 8, 1, None, None, odd, None) == -1
+    assert "aligned" in aenc.last_error()
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the path taken when no device exists")
