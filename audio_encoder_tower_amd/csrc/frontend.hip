@@ -214,6 +214,7 @@ extern "C" aenc_frontend* aenc_frontend_create(const aenc_frontend_config* c) {
 
 extern "C" int aenc_frontend_run(aenc_frontend* h, const float* audio, void* mel_out, void* stream) {
   if (!h || !audio || !mel_out) { fe_error("NULL argument"); return AENC_E_INVAL; }
+  if (((uintptr_t)audio | (uintptr_t)mel_out) & 15) { fe_error("audio and mel must be 16-byte aligned"); return AENC_E_INVAL; }
   const aenc_frontend_config& c = h->cfg;
   hipStream_t s = (hipStream_t)stream;
   const int B = c.batch, n = c.n_samples, F = h->frames, n_mel = c.n_mel;

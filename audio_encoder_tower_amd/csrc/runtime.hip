@@ -590,6 +590,7 @@ extern "C" int aenc_handle_geometry(const aenc_handle* h, aenc_geometry* g) {
 extern "C" int aenc_forward(aenc_handle* h, const void* mel, const uint8_t* mask, void* out, void* stream) {
   if (!h) { set_error("handle is NULL"); return AENC_E_INVAL; }
   if (!mel || !out) { set_error("mel and out must not be NULL"); return AENC_E_INVAL; }
+  if (((uintptr_t)mel | (uintptr_t)out) & 15) { set_error("mel and out must be 16-byte aligned"); return AENC_E_INVAL; }
   const aenc_geometry& g = h->g;
   hipStream_t s = (hipStream_t)stream;
   const int B = g.batch, T = h->T, F = g.n_frames, d = g.d_model, f = g.d_ffn, C = g.n_mel;

@@ -148,10 +148,11 @@ aenc_handle *aenc_create(const aenc_geometry *g, const aenc_weights *w);
  *          positions read may hold anything finite.
  *   out  : device, [batch, T_out, D_out] in out_dtype, with T_out = T /
  *          pool_step and D_out = proj_out or d_model (see aenc_output_shape).
+ * mel and out must be 16-byte aligned (hipMalloc and torch allocations are).
  * Forwards on one handle share its workspace and must be ordered (one stream
- * or explicit dependencies). Returns AENC_OK or AENC_E_INVAL (NULL handle or
- * pointer) or AENC_E_HIP (launch failure); device faults surface at the
- * caller's next synchronisation. */
+ * or explicit dependencies). Returns AENC_OK, AENC_E_INVAL (NULL handle, NULL
+ * or misaligned pointer) or AENC_E_HIP (launch failure); device faults
+ * surface at the caller's next synchronisation. */
 int aenc_forward(aenc_handle *h, const void *mel, const uint8_t *mask, void *out, void *stream);
 
 /* Release the handle's device memory. NULL is ignored. Synchronises the device
@@ -254,9 +255,9 @@ int aenc_frontend_output_shape(const aenc_frontend_config *c, int64_t shape[3]);
 aenc_frontend *aenc_frontend_create(const aenc_frontend_config *c);
 
 /* audio: device fp32 [batch, n_samples]; mel: device [batch, n_mel, frames]
- * in out_dtype, channels first (the layout aenc_forward reads). Enqueues on
- * `stream` without synchronising and allocates nothing. Calls on one handle
- * must be stream-ordered (one workspace). */
+ * in out_dtype, channels first (the layout aenc_forward reads); both 16-byte
+ * aligned. Enqueues on `stream` without synchronising and allocates nothing.
+ * Calls on one handle must be stream-ordered (one workspace). */
 int aenc_frontend_run(aenc_frontend *h, const float *audio, void *mel, void *stream);
 
 /* Free the handle (NULL is accepted). */

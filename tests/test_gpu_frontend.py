@@ -1,4 +1,5 @@
 """GPU log-mel front end (aenc_frontend_*) against the fp64 front-end oracle."""
+import ctypes
 import numpy as np
 import pytest
 import torch
@@ -84,4 +85,9 @@ def test_frontend_rejects_bad_arguments(aenc):
     with pytest.raises(ValueError):
         fe(torch.zeros(1, 16160, device=DEV))
     assert aenc.lib().aenc_frontend_run(fe._h, None, None, None) == -1
+    audio = torch.zeros(16000 + 8, device=DEV)
+    mel = torch.zeros(80 * 100 + 8, device=DEV)
+    assert aenc.lib().aenc_frontend_run(fe._h, ctypes.c_void_p(audio.data_ptr() + 4),
+                                        ctypes.c_void_p(mel.data_ptr()), None) == -1
+    assert "aligned" in aenc.last_error()
     fe.close()

@@ -4,6 +4,8 @@ Reduced geometries are compared element by element on every row; the five
 full-size workloads are compared on sampled clips (each run alone by the
 oracle, clips being independent) and, for the larger ones, sampled rows.
 """
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -267,4 +269,13 @@ def test_forward_rejects_bad_arguments(aenc):
         enc.forward(torch.zeros(1, g.n_mel, g.n_frames, device=DEV, dtype=torch.float32))
     st = aenc.lib().aenc_forward(enc._h, None, None, None, None)
     assert st == -1 and "NULL" in aenc.last_error()
+    # misaligned device pointers are refused before anything is enqueued
+    mel = torch.zeros(1 * g.n_mel * g.n_frames + 8, device=DEV, dtype=torch.bfloat16)
+    out = torch.zeros(1 << 20, device=DEV, dtype=torch.float32)
+    st = aenc.lib().aenc_forward(enc._h, ctypes.c_void_p(mel.data_ptr() + 2), None,
+                                 ctypes.c_void_p(out.data_ptr()), None)
+    assert st == -1 and "aligned" in aenc.last_error()
+    st = aenc.lib().aenc_forward(enc._h, ctypes.c_void_p(mel.data_ptr()), None,
+                                 ctypes.c_void_p(out.data_ptr() + 4), None)
+    assert st == -1 and "aligned" in aenc.last_error()
     enc.close()
