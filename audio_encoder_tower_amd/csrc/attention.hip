@@ -54,17 +54,35 @@ __global__ __launch_bounds__(256) void attention_bf16_kernel(const bf16_t* __res
                                                              const int32_t* __restrict__ lens, int d,
                                                              bf16_t* __restrict__ o, int64_t ld_o,
                                                              const int32_t* __restrict__ key_lo,
-                                                             const int32_t* __restrict__ key_hi) {
+                                                             const int32_t* __restrict__ key_hi, int n_qb,
+                                                             int n_clips) {
   __shared__ __align__(16) bf16_t Ks[2][ATT_BK * ATT_D];   // [key][dim], swizzled 16-byte chunks
   __shared__ __align__(16) bf16_t Vs[2][ATT_D * ATT_BK];   // [dim][key position], swizzled
 
   // RANGED: the grid is (head, clip, query block) with the query blocks in
   // reverse, so the blocks that see the most keys (the last ones under the
   // chunk-causal rule) are dispatched first and the short ones fill in behind.
-  const int b = RANGED ? blockIdx.y : blockIdx.z, h = RANGED ? blockIdx.x : blockIdx.y;
+  // Otherwise the grid is 1-D and each of the 8 XCDs (private L2 each) takes a
+  // contiguous range of (clip, head, query block), query blocks fastest: the
+  // query blocks of one clip and head, which all stream the same K and V, run
+  // together on one XCD and share its L2 (workgroup b runs on XCD b mod 8).
+  int b, h, qb;
+  if (RANGED) {
+    b = blockIdx.y;
+    h = blockIdx.x;
+    qb = gridDim.z - 1 - blockIdx.z;
+  } else {
+    const int n = n_qb * (d / ATT_D) * n_clips;
+    const int per_xcd = gridDim.x / 8;
+    const int L = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+    if (L >= n) return;
+    qb = L % n_qb;
+    h = (L / n_qb) % (d / ATT_D);
+    b = L / (n_qb * (d / ATT_D));
+  }
   const int start = starts[b];
   const int len = lens[b];
-  const int q0 = (RANGED ? gridDim.z - 1 - blockIdx.z : blockIdx.x) * ATT_BQ;
+  const int q0 = qb * ATT_BQ;
   if (q0 >= len) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -307,13 +325,17 @@ hipError_t attention_bf16(const bf16_t* qk, int64_t ld_qk, const bf16_t* vt, int
   // buffer-load offsets within one clip stay below 2^31 bytes
   if ((int64_t)(max_len + ATT_BK) * ld_qk * 2 >= INT32_MAX || (int64_t)ATT_D * ld_vt * 2 >= INT32_MAX)
     return hipErrorInvalidValue;
-  dim3 grid((max_len + ATT_BQ - 1) / ATT_BQ, n_heads, n_clips);
-  if (key_lo)
-    hipLaunchKernelGGL(attention_bf16_kernel<true>, dim3(n_heads, n_clips, grid.x), dim3(256), 0, stream, qk, ld_qk,
-                       vt, ld_vt, start, len, n_heads * ATT_D, o, ld_o, key_lo, key_hi);
-  else
-    hipLaunchKernelGGL(attention_bf16_kernel<false>, grid, dim3(256), 0, stream, qk, ld_qk, vt, ld_vt, start, len,
-                       n_heads * ATT_D, o, ld_o, nullptr, nullptr);
+  const int n_qb = (max_len + ATT_BQ - 1) / ATT_BQ;
+  if (key_lo) {
+    hipLaunchKernelGGL(attention_bf16_kernel<true>, dim3(n_heads, n_clips, n_qb), dim3(256), 0, stream, qk, ld_qk,
+                       vt, ld_vt, start, len, n_heads * ATT_D, o, ld_o, key_lo, key_hi, n_qb, n_clips);
+  } else {
+    const int64_t n = (int64_t)n_qb * n_heads * n_clips;
+    if (n > INT32_MAX - 8) return hipErrorInvalidValue;
+    const int grid = (int)((n + 7) / 8 * 8);
+    hipLaunchKernelGGL(attention_bf16_kernel<false>, dim3(grid), dim3(256), 0, stream, qk, ld_qk, vt, ld_vt, start,
+                       len, n_heads * ATT_D, o, ld_o, nullptr, nullptr, n_qb, n_clips);
+  }
   return hipGetLastError();
 }
 
