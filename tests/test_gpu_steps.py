@@ -91,9 +91,13 @@ def test_gemm_bf16(_lib, shape, epi, tile):
 
 
 @pytest.mark.parametrize("q_scale", [1.0, 0.18033688011112042], ids=["plain", "attention_q_scale"])
-def test_qkv_split_layout(_lib, q_scale):
+@pytest.mark.parametrize("M,d", [(777, 256), (777, 192), (30000, 192)],
+                         ids=["128x128_tiles", "3_heads", "256x256_tiles_3_heads"])
+def test_qkv_split_layout(_lib, q_scale, M, d):
+    """[Q|K] row-major and V^T, with the Q scale. With 3 heads the Q|K / V
+    split (column 384) falls inside a 256-wide tile, whose two waves then take
+    different epilogues (bf16 rows stored from registers, V^T through LDS)."""
     rng = np.random.default_rng(1)
-    M, d = 777, 256
     a = bf16(rng, M, d)
     wqkv = bf16(rng, 3 * d, d, scale=0.05)
     bias = (rng.standard_normal(3 * d) * 0.1).astype(np.float32)
