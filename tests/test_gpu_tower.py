@@ -279,3 +279,41 @@ def test_forward_rejects_bad_arguments(aenc):
                                  ctypes.c_void_p(out.data_ptr() + 4), None)
     assert st == -1 and "aligned" in aenc.last_error()
     enc.close()
+
+
+@pytest.mark.parametrize("masked", [False, True], ids=["dense", "masked"])
+def test_forward_in_hip_graph(aenc, masked):
+    """aenc_forward enqueues without allocating or synchronising, so it can be
+    captured into a HIP graph. Every replay (with eager forwards on the same
+    handle in between) matches the eager result bit for bit."""
+    w = reduced("whisper_large_b1", "graph", dict(n_layers=2, n_frames=400, batch=2), init="perturbed")
+    g = w.geom
+    enc = aenc.Encoder(g, device_weights(synth.make_weights(w), g.dtype))
+    mel = torch.from_numpy(synth.make_mel(w)).to(DEV).to(torch.bfloat16)
+    mask = None
+    if masked:
+        m = np.ones((g.batch, g.n_frames // 2), np.uint8)
+        m[1, 130:] = 0
+        mask = torch.from_numpy(m).to(DEV)
+    ref = enc.forward(mel, mask).clone()
+    torch.cuda.synchronize()
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        enc.forward(mel, mask)                  # warm-up on a side stream, as torch asks before capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    out = torch.empty_like(ref)
+    with torch.cuda.graph(graph):
+        enc.forward(mel, mask, out=out)
+    for _ in range(3):
+        out.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref)
+        eager = enc.forward(mel, mask)
+        torch.cuda.synchronize()
+        assert torch.equal(eager, ref)
+    enc.close()
