@@ -55,7 +55,7 @@ class Encoder:
 
     geom: an object with the aenc_geometry fields (batch, n_mel, n_frames,
       d_model, n_layers, n_heads, d_ffn, pool_step, proj_hidden, proj_out,
-      dtype, out_dtype, ln_eps, stack).
+      dtype, out_dtype, ln_eps, stack, attn_chunk, attn_chunk_mode).
     weights: name -> tensor (host or device, contiguous, the geometry's
       dtype); names conv1_w, conv1_b, conv2_w, conv2_b,
       layers.{l}.{ln1_g, ln1_b, q_w, q_b, k_w, v_w, v_b, o_w, o_b, ln2_g, ln2_b,
