@@ -170,6 +170,28 @@ extern "C" int aenc_validate(const aenc_geometry* g) {
               g->attn_chunk_mode);
     return AENC_E_INVAL;
   }
+  if (g->dtype == AENC_BF16) {
+    // The bf16 GEMMs copy A and W through buffer resources, whose byte offsets
+    // are 32-bit: every operand must stay under 4 GiB. Per clip, the largest A
+    // operands are the conv stem's padded frames and the FFN (or projector)
+    // hidden rows.
+    const int64_t lim = (int64_t)UINT32_MAX;
+    const int64_t F2 = g->n_frames + 2, T8 = round_up(g->n_frames / 2, 8), d = g->d_model;
+    const int64_t mid = std::max<int64_t>(g->d_ffn, g->proj_hidden);
+    const int64_t per_clip = 2 * std::max({F2 * round_up(g->n_mel, 64), F2 * d, T8 * mid});
+    if ((int64_t)g->batch * per_clip >= lim) {
+      set_error("batch %d: a bf16 GEMM operand would span %lld bytes, over the 4 GiB that 32-bit buffer offsets "
+                "reach; at most %lld clips of this geometry per forward",
+                g->batch, (long long)(g->batch * per_clip), (long long)((lim - 1) / per_clip));
+      return AENC_E_INVAL;
+    }
+    const int64_t proj_in = d * std::max(1, g->stack);
+    if (proj && (2 * g->proj_hidden * proj_in >= lim || 2 * (int64_t)g->proj_out * g->proj_hidden >= lim)) {
+      set_error("projector weights of %d x %lld and %d x %d bf16 must each stay under 4 GiB", g->proj_hidden,
+                (long long)proj_in, g->proj_out, g->proj_hidden);
+      return AENC_E_INVAL;
+    }
+  }
   return AENC_OK;
 }
 

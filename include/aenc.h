@@ -70,7 +70,10 @@ typedef enum {
  * records print (d_model, encoder_layers, encoder_attention_heads,
  * encoder_ffn_dim, num_mel_bins, audio_pool_step, projector width). */
 typedef struct aenc_geometry {
-  int32_t batch;        /* clips per forward; the workspace is sized for it (>= 1)          */
+  int32_t batch;        /* clips per forward, 1 .. 4096; the workspace is sized for it.
+                         * bf16: each GEMM operand must stay under 4 GiB (32-bit buffer
+                         * offsets), e.g. at most 278 clips of 3000 frames with d_ffn
+                         * 5120; aenc_validate reports the largest batch allowed.     */
   int32_t n_mel;        /* num_mel_bins (1 .. 512)                                           */
   int32_t n_frames;     /* F mel frames per clip, even, 2 .. 3000; T = F/2 positions         */
   int32_t d_model;      /* d = 64 * n_heads, a multiple of 128, <= 2048                       */
@@ -126,7 +129,9 @@ typedef struct aenc_weights {
 typedef struct aenc_handle aenc_handle;
 
 /* Check a geometry on the host. No device call. Returns AENC_OK, AENC_E_INVAL
- * or AENC_E_UNSUPPORTED (pool_step 2 together with a projector: the pages never
+ * (a field out of range, or a bf16 batch whose largest GEMM operand would
+ * reach 4 GiB: aenc_last_error() names the largest batch allowed) or
+ * AENC_E_UNSUPPORTED (pool_step 2 together with a projector: the pages never
  * combine them, so their order is not defined). */
 int aenc_validate(const aenc_geometry *g);
 

@@ -89,6 +89,23 @@ def test_invalid_geometries_are_rejected(aenc, case):
     assert aenc.lib().aenc_param_count(ctypes.byref(aenc._lib.geometry(g.replace(**kw)))) == -1
 
 
+def test_bf16_batch_limit_of_32_bit_gemm_offsets(aenc):
+    """The bf16 GEMMs reach their operands through 32-bit byte offsets. For
+    Whisper-large the FFN hidden rows are the largest operand: 1504 padded rows
+    x 5120 x 2 bytes = 15,400,960 bytes per clip, so 278 clips fit under
+    4 GiB and 279 do not; validation names the limit."""
+    g = synth.get_workload("whisper_large_b1").geom
+    assert aenc.validate(g.replace(batch=278)) == 0
+    assert aenc.validate(g.replace(batch=279)) == -1
+    assert "at most 278 clips" in aenc.last_error()
+    # a projector hidden width above d_ffn sets the limit instead
+    gp = g.replace(proj_hidden=8192, proj_out=64)
+    per_clip = 1504 * 8192 * 2
+    ok = (2**32 - 2) // per_clip
+    assert aenc.validate(gp.replace(batch=ok)) == 0
+    assert aenc.validate(gp.replace(batch=ok + 1)) == -1
+
+
 def test_pool_with_projector_is_unsupported(aenc):
     g = synth.get_workload("whisper_medium_pool2_b1").geom.replace(proj_hidden=128, proj_out=128)
     assert aenc.validate(g) == -2
