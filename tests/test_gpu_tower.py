@@ -223,6 +223,33 @@ def test_deterministic_and_batch_independent(aenc):
     np.testing.assert_array_equal(a[1], c[0])
 
 
+def test_forward_at_the_bf16_batch_limit(aenc):
+    """The largest Whisper-large bf16 batch that validation accepts (278
+    clips): the FFN hidden rows then span 4,281,466,880 bytes, so the GEMM
+    copies of the last clips use buffer offsets above 2^31. The same clip is
+    repeated; every copy of it must come out bit-identical to the first and
+    match the oracle."""
+    w = synth.get_workload("whisper_large_b1")
+    W = synth.make_weights(w)
+    g = w.geom.replace(batch=278)
+    assert aenc.validate(g) == 0 and aenc.validate(g.replace(batch=279)) == -1
+    print(f"gpu forward whisper_large_b1 x 278 geom={g}", flush=True)
+    enc = aenc.Encoder(g, device_weights(W, g.dtype))
+    mel1 = torch.from_numpy(synth.make_mel(w)).to(DEV).to(torch.bfloat16)
+    mel = mel1.expand(g.batch, -1, -1).contiguous()
+    out = enc.forward(mel)
+    torch.cuda.synchronize()
+    picks = [0, 139, 276, 277]
+    got = out[picks].float().cpu().numpy().astype(np.float64)
+    del out, mel
+    enc.close()
+    for i in range(1, len(picks)):
+        np.testing.assert_array_equal(got[i], got[0], err_msg=f"clip {picks[i]} differs from clip 0")
+    ref = parity.oracle_clip(w, 0, W, every=1)
+    m = parity.assert_bf16_parity(got[-1][ref["rows"]], ref["out"], "batch 278, clip 277")
+    print("batch limit", m, flush=True)
+
+
 def test_padded_frames_do_not_change_valid_rows(aenc):
     w = reduced("whisper_large_varlen_b32", "pad", dict(batch=2, n_layers=2, n_frames=1200), init="perturbed")
     W = synth.make_weights(w)
