@@ -46,6 +46,7 @@ namespace aenc {
 constexpr int GEMM_BK = 64;
 constexpr int GEMM_GROUP_M = 4;
 constexpr int N_XCD = 8;
+constexpr int CUS_PER_XCD = 32;
 
 struct GemmArgs {
   const bf16_t* A;
@@ -57,6 +58,10 @@ struct GemmArgs {
   uint32_t a_bytes, w_bytes;   // extents of A and W reachable through the row maps
   int tiles_m, tiles_n, grid;
   EpiParams epi;
+  // 256x256 kernel with a split tail: each XCD takes tiles_per_xcd tiles,
+  // runs the first split_full whole and the rest as two 256x128 halves
+  // (split_full = 0: no split, grid / N_XCD whole tiles per XCD)
+  int tiles_per_xcd, split_full;
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -111,13 +116,9 @@ __device__ __forceinline__ void mma(f32x16 (&acc)[SM][SN], const bf16x8 (&fa)[SM
     for (int j = 0; j < SN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
 }
 
-// Tile (tm, tn) of workgroup blockIdx.x: XCD-contiguous ranges, then
-// GROUP_M-tall groups walked column by column. False for padding workgroups.
-__device__ __forceinline__ bool tile_of_block(const GemmArgs& g, int& tm, int& tn) {
-  const int total = g.tiles_m * g.tiles_n;
-  const int per_xcd = g.grid / N_XCD;
-  const int tile = (blockIdx.x % N_XCD) * per_xcd + blockIdx.x / N_XCD;
-  if (tile >= total) return false;
+// Tile index (XCD-contiguous) -> (tm, tn): GROUP_M-tall groups walked column
+// by column.
+__device__ __forceinline__ void tile_group_order(const GemmArgs& g, int tile, int& tm, int& tn) {
   const int group_size = GEMM_GROUP_M * g.tiles_n;
   const int group = tile / group_size;
   const int first_m = group * GEMM_GROUP_M;
@@ -125,6 +126,33 @@ __device__ __forceinline__ bool tile_of_block(const GemmArgs& g, int& tm, int& t
   const int in_group = tile - group * group_size;
   tm = first_m + in_group % gm;
   tn = in_group / gm;
+}
+
+// Tile (tm, tn) of workgroup blockIdx.x: XCD-contiguous ranges of tiles, in
+// group order. False for padding workgroups.
+__device__ __forceinline__ bool tile_of_block(const GemmArgs& g, int& tm, int& tn) {
+  const int per_xcd = g.grid / N_XCD;
+  const int tile = (blockIdx.x % N_XCD) * per_xcd + blockIdx.x / N_XCD;
+  if (tile >= g.tiles_m * g.tiles_n) return false;
+  tile_group_order(g, tile, tm, tn);
+  return true;
+}
+
+// The same for the 256x256 kernel, whose tail may be split: half is -1 for a
+// whole tile, else which 128-column half of tile (tm, tn) the workgroup
+// takes. When an XCD's tiles leave a last round of at most 16 on its 32 CUs,
+// halving those tiles spreads that round over twice as many CUs.
+__device__ __forceinline__ bool big_tile_of_block(const GemmArgs& g, int& tm, int& tn, int& half) {
+  half = -1;
+  if (g.split_full == 0) return tile_of_block(g, tm, tn);
+  const int x = blockIdx.x % N_XCD, i = blockIdx.x / N_XCD;
+  int tile = x * g.tiles_per_xcd + i;
+  if (i >= g.split_full) {
+    tile = x * g.tiles_per_xcd + g.split_full + (i - g.split_full) / 2;
+    half = (i - g.split_full) & 1;
+  }
+  if (tile >= g.tiles_m * g.tiles_n) return false;
+  tile_group_order(g, tile, tm, tn);
   return true;
 }
 
@@ -413,43 +441,68 @@ typedef int i32x4_asm __attribute__((ext_vector_type(4)));
 template <int SM, int SN>
 __device__ __forceinline__ void read_half_wait(const bf16_t* as, const bf16_t* bs, int a_row0, int b_row0, int sw,
                                                int fk, int h, bf16x8 (&fa)[2][SM], bf16x8 (&fb)[2][SN]) {
-  static_assert(SM == 2 && SN == 4, "written for the 64x128 wave tile");
+  static_assert(SM == 2 && (SN == 4 || SN == 2), "written for the 64x128 and 64x64 wave tiles");
   const uint32_t ab = (uint32_t)(uintptr_t)(lds_void*)as, bb = (uint32_t)(uintptr_t)(lds_void*)bs;
   const uint32_t pa0 = ab + (a_row0 * GEMM_BK + ((4 * h + 0 + fk) ^ sw) * 8) * 2;
   const uint32_t pa1 = ab + (a_row0 * GEMM_BK + ((4 * h + 2 + fk) ^ sw) * 8) * 2;
   const uint32_t pb0 = bb + (b_row0 * GEMM_BK + ((4 * h + 0 + fk) ^ sw) * 8) * 2;
   const uint32_t pb1 = bb + (b_row0 * GEMM_BK + ((4 * h + 2 + fk) ^ sw) * 8) * 2;
-  i32x4_asm r[12];
-  asm volatile(
-      "ds_read_b128 %0, %12\n"
-      "ds_read_b128 %1, %12 offset:4096\n"
-      "ds_read_b128 %2, %13\n"
-      "ds_read_b128 %3, %13 offset:4096\n"
-      "ds_read_b128 %4, %13 offset:8192\n"
-      "ds_read_b128 %5, %13 offset:12288\n"
-      "ds_read_b128 %6, %14\n"
-      "ds_read_b128 %7, %14 offset:4096\n"
-      "ds_read_b128 %8, %15\n"
-      "ds_read_b128 %9, %15 offset:4096\n"
-      "ds_read_b128 %10, %15 offset:8192\n"
-      "ds_read_b128 %11, %15 offset:12288\n"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7]),
-        "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11])
-      : "v"(pa0), "v"(pb0), "v"(pa1), "v"(pb1)
-      : "memory");
-  fa[0][0] = __builtin_bit_cast(bf16x8, r[0]);
-  fa[0][1] = __builtin_bit_cast(bf16x8, r[1]);
-  fb[0][0] = __builtin_bit_cast(bf16x8, r[2]);
-  fb[0][1] = __builtin_bit_cast(bf16x8, r[3]);
-  fb[0][2] = __builtin_bit_cast(bf16x8, r[4]);
-  fb[0][3] = __builtin_bit_cast(bf16x8, r[5]);
-  fa[1][0] = __builtin_bit_cast(bf16x8, r[6]);
-  fa[1][1] = __builtin_bit_cast(bf16x8, r[7]);
-  fb[1][0] = __builtin_bit_cast(bf16x8, r[8]);
-  fb[1][1] = __builtin_bit_cast(bf16x8, r[9]);
-  fb[1][2] = __builtin_bit_cast(bf16x8, r[10]);
-  fb[1][3] = __builtin_bit_cast(bf16x8, r[11]);
+  if constexpr (SN == 2) {
+    i32x4_asm r[8];
+    asm volatile(
+        "ds_read_b128 %0, %8\n"
+        "ds_read_b128 %1, %8 offset:4096\n"
+        "ds_read_b128 %2, %9\n"
+        "ds_read_b128 %3, %9 offset:4096\n"
+        "ds_read_b128 %4, %10\n"
+        "ds_read_b128 %5, %10 offset:4096\n"
+        "ds_read_b128 %6, %11\n"
+        "ds_read_b128 %7, %11 offset:4096\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+        : "v"(pa0), "v"(pb0), "v"(pa1), "v"(pb1)
+        : "memory");
+    fa[0][0] = __builtin_bit_cast(bf16x8, r[0]);
+    fa[0][1] = __builtin_bit_cast(bf16x8, r[1]);
+    fb[0][0] = __builtin_bit_cast(bf16x8, r[2]);
+    fb[0][1] = __builtin_bit_cast(bf16x8, r[3]);
+    fa[1][0] = __builtin_bit_cast(bf16x8, r[4]);
+    fa[1][1] = __builtin_bit_cast(bf16x8, r[5]);
+    fb[1][0] = __builtin_bit_cast(bf16x8, r[6]);
+    fb[1][1] = __builtin_bit_cast(bf16x8, r[7]);
+  } else {
+    i32x4_asm r[12];
+    asm volatile(
+        "ds_read_b128 %0, %12\n"
+        "ds_read_b128 %1, %12 offset:4096\n"
+        "ds_read_b128 %2, %13\n"
+        "ds_read_b128 %3, %13 offset:4096\n"
+        "ds_read_b128 %4, %13 offset:8192\n"
+        "ds_read_b128 %5, %13 offset:12288\n"
+        "ds_read_b128 %6, %14\n"
+        "ds_read_b128 %7, %14 offset:4096\n"
+        "ds_read_b128 %8, %15\n"
+        "ds_read_b128 %9, %15 offset:4096\n"
+        "ds_read_b128 %10, %15 offset:8192\n"
+        "ds_read_b128 %11, %15 offset:12288\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7]),
+          "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11])
+        : "v"(pa0), "v"(pb0), "v"(pa1), "v"(pb1)
+        : "memory");
+    fa[0][0] = __builtin_bit_cast(bf16x8, r[0]);
+    fa[0][1] = __builtin_bit_cast(bf16x8, r[1]);
+    fb[0][0] = __builtin_bit_cast(bf16x8, r[2]);
+    fb[0][1] = __builtin_bit_cast(bf16x8, r[3]);
+    fb[0][2] = __builtin_bit_cast(bf16x8, r[4]);
+    fb[0][3] = __builtin_bit_cast(bf16x8, r[5]);
+    fa[1][0] = __builtin_bit_cast(bf16x8, r[6]);
+    fa[1][1] = __builtin_bit_cast(bf16x8, r[7]);
+    fb[1][0] = __builtin_bit_cast(bf16x8, r[8]);
+    fb[1][1] = __builtin_bit_cast(bf16x8, r[9]);
+    fb[1][2] = __builtin_bit_cast(bf16x8, r[10]);
+    fb[1][3] = __builtin_bit_cast(bf16x8, r[11]);
+  }
 }
 
 template <int SM, int SN>
@@ -465,12 +518,14 @@ struct BigCopy {
   __amdgpu_buffer_rsrc_t ra, rw;
   CopyPlan<4> pa, pw;
   int wave;
+  bool w_on;   // uniform: false for the waves whose W rows lie outside a half tile
   // this wave's 4 copy instructions of the A (or W) part of the slice at K byte offset k_bytes
   __device__ __forceinline__ void slice_a(uint32_t k_bytes, bf16_t* la) const {
 #pragma unroll
     for (int i = 0; i < 4; ++i) copy16(ra, la + (wave * 4 + i) * 8 * GEMM_BK, pa.off[i], k_bytes);
   }
   __device__ __forceinline__ void slice_w(uint32_t k_bytes, bf16_t* lw) const {
+    if (!w_on) return;
 #pragma unroll
     for (int i = 0; i < 4; ++i) copy16(rw, lw + (wave * 4 + i) * 8 * GEMM_BK, pw.off[i], k_bytes);
   }
@@ -564,22 +619,14 @@ __device__ __forceinline__ void big_loop(f32x16 (&acc)[SM][SN], bf16_t* a0, bf16
   AENC_BARRIER();
 }
 
-template <int EPI>
-__global__ __launch_bounds__(BIG_THREADS) void gemm_bf16_256_kernel(GemmArgs g) {
-  constexpr int BM = 256, BN = 256, WM = 64, WN = 128;
-  constexpr int SM = WM / 32, SN = WN / 32;
-  __shared__ __attribute__((aligned(16))) bf16_t la0[BM * GEMM_BK];
-  __shared__ __attribute__((aligned(16))) bf16_t la1[BM * GEMM_BK];
-  __shared__ __attribute__((aligned(16))) bf16_t la2[BM * GEMM_BK];
-  __shared__ __attribute__((aligned(16))) bf16_t lw0[BN * GEMM_BK];
-  __shared__ __attribute__((aligned(16))) bf16_t lw1[BN * GEMM_BK];
-
-  int tm, tn;
-  if (!tile_of_block(g, tm, tn)) return;
-  const int M = g.m_dev ? *g.m_dev : g.M;
-  const int m0 = tm * BM, n0 = tn * BN;
-  if (m0 >= M) return;
-
+// One 256-row tile of C, 256 columns wide (SN 4: 64x128 per wave) or, for a
+// split tail, 128 wide (SN 2: 64x64 per wave; only waves 0-3 copy W, whose
+// 128 rows fill the first half of each W buffer).
+template <int EPI, int SN>
+__device__ __forceinline__ void big_tile(const GemmArgs& g, int m0, int n0, int M, bf16_t* la0, bf16_t* la1,
+                                         bf16_t* la2, bf16_t* lw0, bf16_t* lw1) {
+  constexpr int WM = 64, WN = 32 * SN;
+  constexpr int SM = WM / 32;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   BigCopy cp;
@@ -588,6 +635,7 @@ __global__ __launch_bounds__(BIG_THREADS) void gemm_bf16_256_kernel(GemmArgs g) 
   cp.pa = plan_a<4>(g, m0, M, wave, lane);
   cp.pw = plan_w<4>(g, n0, wave, lane);
   cp.wave = wave;
+  cp.w_on = SN == 4 || wave < 4;
 
   f32x16 acc[SM][SN];
 #pragma unroll
@@ -622,6 +670,30 @@ __global__ __launch_bounds__(BIG_THREADS) void gemm_bf16_256_kernel(GemmArgs g) 
   store_tile<EPI, SM, SN, SW>(g, acc, slab, m0 + wm * WM, n0 + wn * WN, lane, M);
 }
 
+// SPLIT: the launch has a split tail (a separate instantiation, so that
+// launches without one run the whole-tile code alone).
+template <int EPI, bool SPLIT>
+__global__ __launch_bounds__(BIG_THREADS) void gemm_bf16_256_kernel(GemmArgs g) {
+  constexpr int BM = 256, BN = 256;
+  __shared__ __attribute__((aligned(16))) bf16_t la0[BM * GEMM_BK];
+  __shared__ __attribute__((aligned(16))) bf16_t la1[BM * GEMM_BK];
+  __shared__ __attribute__((aligned(16))) bf16_t la2[BM * GEMM_BK];
+  __shared__ __attribute__((aligned(16))) bf16_t lw0[BN * GEMM_BK];
+  __shared__ __attribute__((aligned(16))) bf16_t lw1[BN * GEMM_BK];
+
+  int tm, tn, half = -1;
+  if (!(SPLIT ? big_tile_of_block(g, tm, tn, half) : tile_of_block(g, tm, tn))) return;
+  const int M = g.m_dev ? *g.m_dev : g.M;
+  const int m0 = tm * BM, n0 = tn * BN;
+  if (m0 >= M) return;
+  if (!SPLIT || half < 0) {
+    big_tile<EPI, 4>(g, m0, n0, M, la0, la1, la2, lw0, lw1);
+  } else {
+    if (n0 + 128 * half >= g.N) return;
+    big_tile<EPI, 2>(g, m0, n0 + 128 * half, M, la0, la1, la2, lw0, lw1);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
@@ -632,8 +704,21 @@ static hipError_t launch_epi(GemmArgs g, int tile_cfg, hipStream_t stream) {
   g.tiles_n = (g.N + bt - 1) / bt;
   const int total = g.tiles_m * g.tiles_n;
   g.grid = (total + N_XCD - 1) / N_XCD * N_XCD;
-  if (tile_cfg == GEMM_TILE_256x256)
-    hipLaunchKernelGGL((gemm_bf16_256_kernel<EPI>), dim3(g.grid), dim3(BIG_THREADS), 0, stream, g);
+  g.tiles_per_xcd = 0;
+  g.split_full = 0;
+  if (tile_cfg == GEMM_TILE_256x256 && total % N_XCD == 0) {
+    // a last round of at most half the XCD's CUs runs as half tiles
+    const int per = total / N_XCD, tail = per % CUS_PER_XCD;
+    if (per > CUS_PER_XCD && tail > 0 && 2 * tail <= CUS_PER_XCD) {
+      g.tiles_per_xcd = per;
+      g.split_full = per - tail;
+      g.grid = N_XCD * (per + tail);
+    }
+  }
+  if (tile_cfg == GEMM_TILE_256x256 && g.split_full == 0)
+    hipLaunchKernelGGL((gemm_bf16_256_kernel<EPI, false>), dim3(g.grid), dim3(BIG_THREADS), 0, stream, g);
+  else if (tile_cfg == GEMM_TILE_256x256)
+    hipLaunchKernelGGL((gemm_bf16_256_kernel<EPI, true>), dim3(g.grid), dim3(BIG_THREADS), 0, stream, g);
   else
     hipLaunchKernelGGL((gemm_bf16_128_kernel<EPI>), dim3(g.grid), dim3(SMALL_THREADS), 0, stream, g);
   return hipGetLastError();

@@ -55,6 +55,7 @@ GEMM_SHAPES = [
     (3000, 1280, 5120),   # FC2
     (777, 1284, 4160),    # ragged M and N, 65 slices: a partial trip of the 6-slice buffer cycle
     (70, 196, 64),        # N = 4 mod 8: 4-column tails and rows not 16-byte aligned
+    (4000, 4920, 1280),   # 256x256: 40 tiles per XCD, the last 8 run as 128-column halves (ragged M, N)
 ]
 
 
@@ -91,8 +92,8 @@ def test_gemm_bf16(_lib, shape, epi, tile):
 
 
 @pytest.mark.parametrize("q_scale", [1.0, 0.18033688011112042], ids=["plain", "attention_q_scale"])
-@pytest.mark.parametrize("M,d", [(777, 256), (777, 192), (30000, 192)],
-                         ids=["128x128_tiles", "3_heads", "256x256_tiles_3_heads"])
+@pytest.mark.parametrize("M,d", [(777, 256), (777, 192), (30000, 192), (8448, 640)],
+                         ids=["128x128_tiles", "3_heads", "256x256_tiles_3_heads", "256x256_split_tail_10_heads"])
 def test_qkv_split_layout(_lib, q_scale, M, d):
     """[Q|K] row-major and V^T, with the Q scale. With 3 heads the Q|K / V
     split (column 384) falls inside a 256-wide tile, whose two waves then take
