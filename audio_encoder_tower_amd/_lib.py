@@ -78,6 +78,8 @@ SIGNATURES = {
     "aenc_k_row_maps": (c_int, [c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                 c_void_p]),
     "aenc_k_copy": (c_int, [c_void_p, c_void_p, c_int64, c_void_p]),
+    "aenc_k_copy_stream": (c_int, [c_void_p, c_void_p, c_int64, c_void_p]),
+    "aenc_k_mfma_loop": (c_int, [c_void_p, c_int, c_int, c_void_p]),
     "aenc_handle_geometry": (c_int, [c_void_p, POINTER(Geometry)]),
     # embeddings cache (aenc.h)
     "aenc_cache_create": (c_void_p, [c_int64, c_int64]),

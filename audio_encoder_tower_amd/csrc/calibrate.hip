@@ -1,0 +1,87 @@
+// Calibration kernels: the ceilings the encoder's kernels are measured against
+// on the part itself, beside the published peaks.
+//   * a streaming copy (16-byte vectors, four in flight per lane): the HBM
+//     read+write rate a plain bandwidth-bound kernel reaches;
+//   * a matrix-core loop: chains of v_mfma_f32_32x32x16_bf16 on register
+//     operands (no memory traffic), the bf16 MFMA rate the part sustains. The
+//     operands are non-zero bf16 values whose mantissa bits change every
+//     iteration, since the matrix cores draw less power, and clock higher, on
+//     zeros or constant inputs than on the varied data of a real product.
+#include "common.h"
+#include "launch.h"
+
+namespace aenc {
+
+__global__ __launch_bounds__(256) void copy4_kernel(u32x4* __restrict__ dst, const u32x4* __restrict__ src,
+                                                    int64_t n16) {
+  const int64_t stride = (int64_t)gridDim.x * 1024;
+  for (int64_t base = (int64_t)blockIdx.x * 1024 + threadIdx.x; base < n16; base += stride) {
+    u32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t i = base + 256 * u;
+      v[u] = i < n16 ? src[i] : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t i = base + 256 * u;
+      if (i < n16) dst[i] = v[u];
+    }
+  }
+}
+
+hipError_t copy_stream(void* dst, const void* src, int64_t bytes, hipStream_t stream) {
+  if (bytes <= 0 || bytes % 16 != 0) return hipErrorInvalidValue;
+  const int64_t n16 = bytes / 16;
+  const int64_t blocks = std::min<int64_t>((n16 + 1023) / 1024, 8192);
+  hipLaunchKernelGGL(copy4_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (u32x4*)dst, (const u32x4*)src, n16);
+  return hipGetLastError();
+}
+
+constexpr int MFMA_CHAINS = 4;
+
+// Each wave runs `iters` rounds of MFMA_CHAINS independent 32x32x16 MFMAs and
+// writes one sum per lane to out[global thread id].
+__global__ __launch_bounds__(256) void mfma_loop_kernel(float* __restrict__ out, int iters) {
+  const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // bf16 pairs with exponent 126..127 (values in [0.5, 2)) and lane-dependent
+  // signs and mantissas
+  uint32_t sa[4], sb[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t h = (lane * 2654435761u) ^ ((uint32_t)i * 40503u) ^ (wave * 97u) ^ (blockIdx.x * 7919u);
+    sa[i] = 0x3F003F00u | (h & 0x807F807Fu);
+    sb[i] = 0x3F003F00u | ((h >> 7) & 0x807F807Fu);
+  }
+  f32x16 acc[MFMA_CHAINS];
+#pragma unroll
+  for (int c = 0; c < MFMA_CHAINS; ++c)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[c][v] = 0.0f;
+  for (int it = 0; it < iters; ++it) {
+    const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{sa[0], sa[1], sa[2], sa[3]});
+    const bf16x8 b = __builtin_bit_cast(bf16x8, u32x4{sb[0], sb[1], sb[2], sb[3]});
+#pragma unroll
+    for (int c = 0; c < MFMA_CHAINS; ++c) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
+    // new mantissas and signs for the next round (exponents unchanged: finite values)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sa[i] ^= 0x80558055u;
+      sb[i] ^= 0x002A802Au;
+    }
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int c = 0; c < MFMA_CHAINS; ++c)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) s += acc[c][v];
+  out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+hipError_t mfma_loop(float* out, int blocks, int iters, hipStream_t stream) {
+  if (blocks < 1 || iters < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(mfma_loop_kernel, dim3(blocks), dim3(256), 0, stream, out, iters);
+  return hipGetLastError();
+}
+
+}  // namespace aenc

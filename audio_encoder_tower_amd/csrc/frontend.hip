@@ -11,16 +11,21 @@
 //
 // On the device:
 //   1. reflect padding of each clip into a workspace row of n_samples + 400;
-//   2. the windowed DFT as an fp32 GEMM whose A rows are the overlapping
-//      frames (a strided row map over the padded clip: no frame copies) and
-//      whose B rows are w[n] cos(2 pi k n / 400) and w[n] sin(...) for bins
-//      k = 0..200 (404 rows, two of them zero);
-//   3. the power |X|^2 into rows of 208 (bins past 200 zero);
-//   4. the mel filters as a second fp32 GEMM (K = 208);
-//   5. log10 with the floor, a per-clip maximum, then the 80 dB floor, the
+//   2. the windowed DFT and the power spectrum in one kernel: a GEMM in fp64
+//      on the vector ALUs whose A rows are the overlapping frames (read
+//      straight from the padded clip, fp32 samples widened to fp64) and whose
+//      B rows are w[n] cos(2 pi k n / 400) and w[n] sin(...) interleaved
+//      (bin k in columns 2k and 2k + 1), so one thread holds the real and
+//      imaginary parts of its bins and writes |X|^2 (rounded to fp32) into
+//      rows of 224 (bins past 200 zero). fp64 sums keep spectral valleys next
+//      to loud bins exact: in fp32 a bin 80 dB under its frame's energy loses
+//      about 1e-3 of its power to cancellation;
+//   3. the mel filters as an fp32 GEMM (K = 224; sums of non-negative terms,
+//      accurate to a few fp32 ulps);
+//   4. log10 with the floor, a per-clip maximum, then the 80 dB floor, the
 //      affine map and a transpose to [B, n_mel, frames] through LDS tiles.
-// The DFT matrix and the filters are built once, in double precision, at
-// create time.
+// The DFT matrix (fp64) and the filters are built once, in double precision,
+// at create time.
 #include <cmath>
 #include <cstring>
 #include <vector>
@@ -41,8 +46,8 @@ using namespace aenc;
 constexpr int FE_NFFT = 400;
 constexpr int FE_HOP = 160;
 constexpr int FE_BINS = FE_NFFT / 2 + 1;   // 201
-constexpr int FE_DFT_N = 404;              // cos rows 0..200, sin rows 201..401, 2 zero rows
-constexpr int FE_PK = 208;                 // power row stride (bins, zero padded to a multiple of 16)
+constexpr int FE_PK = 224;                 // bins in a power row: 201, zero padded to 7 tiles of 32
+constexpr int FE_DFT_N = 2 * FE_PK;        // DFT matrix rows: cos and sin of each (padded) bin, interleaved
 
 __global__ void reflect_pad_kernel(const float* __restrict__ x, float* __restrict__ xp, int n, int B) {
   const int padded = n + FE_NFFT;
@@ -56,17 +61,71 @@ __global__ void reflect_pad_kernel(const float* __restrict__ x, float* __restric
   }
 }
 
-__global__ void power_kernel(const float* __restrict__ X, float* __restrict__ P, int64_t rows) {
-  const int64_t total = rows * FE_PK;
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t r = i / FE_PK;
-    const int k = (int)(i - r * FE_PK);
-    float p = 0.0f;
-    if (k < FE_BINS) {
-      const float re = X[r * FE_DFT_N + k], im = X[r * FE_DFT_N + FE_BINS + k];
-      p = fmaf(re, re, im * im);
+// Power spectrum of the frames: P[r, k] = (sum_n x_r[n] C[2k, n])^2 + (sum_n x_r[n] C[2k+1, n])^2
+// in fp64, stored as fp32. Frame r = b F + f reads padded samples [b n_pad + 160 f, + 400).
+// A workgroup takes 128 frames x 64 DFT columns (32 bins); thread (ty, tx) holds
+// frames 8 ty .. 8 ty + 7 and columns 4 tx .. 4 tx + 3 (bins 2 tx and 2 tx + 1 of the tile).
+// K advances 16 samples at a time through LDS, k-major.
+constexpr int DP_BM = 128, DP_BN = 64, DP_BK = 16;
+
+__global__ __launch_bounds__(256) void dft_power_kernel(const float* __restrict__ xp, int n_pad, int F, int rows,
+                                                        const double* __restrict__ dft, float* __restrict__ P) {
+  __shared__ __attribute__((aligned(16))) double As[DP_BK][DP_BM + 2];
+  __shared__ __attribute__((aligned(16))) double Bs[DP_BK][DP_BN + 2];
+  const int m0 = blockIdx.y * DP_BM, n0 = blockIdx.x * DP_BN;
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  // A loader: frame m0 + (tid >> 1), samples 8 (tid & 1) .. +7 of the slice
+  const int ar = tid >> 1, ak = (tid & 1) * 8;
+  const int r_ld = min(m0 + ar, rows - 1);
+  const int b_ld = r_ld / F;
+  const float* a_src = xp + (int64_t)b_ld * n_pad + (int64_t)FE_HOP * (r_ld - b_ld * F) + ak;
+  // B loader: DFT row n0 + (tid >> 2), samples 4 (tid & 3) .. +3 of the slice
+  const int br = tid >> 2, bk = (tid & 3) * 4;
+  const double* b_src = dft + (int64_t)(n0 + br) * FE_NFFT + bk;
+
+  double acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
+
+  for (int k0 = 0; k0 < FE_NFFT; k0 += DP_BK) {
+    const float4 a0 = *(const float4*)(a_src + k0);
+    const float4 a1 = *(const float4*)(a_src + k0 + 4);
+    const double2 b0 = *(const double2*)(b_src + k0);
+    const double2 b1 = *(const double2*)(b_src + k0 + 2);
+    As[ak + 0][ar] = a0.x; As[ak + 1][ar] = a0.y; As[ak + 2][ar] = a0.z; As[ak + 3][ar] = a0.w;
+    As[ak + 4][ar] = a1.x; As[ak + 5][ar] = a1.y; As[ak + 6][ar] = a1.z; As[ak + 7][ar] = a1.w;
+    Bs[bk + 0][br] = b0.x; Bs[bk + 1][br] = b0.y; Bs[bk + 2][br] = b1.x; Bs[bk + 3][br] = b1.y;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < DP_BK; ++k) {
+      double av[8], bv[4];
+#pragma unroll
+      for (int i = 0; i < 8; i += 2) {
+        const double2 t = *(const double2*)&As[k][ty * 8 + i];
+        av[i] = t.x;
+        av[i + 1] = t.y;
+      }
+      const double2 u0 = *(const double2*)&Bs[k][tx * 4];
+      const double2 u1 = *(const double2*)&Bs[k][tx * 4 + 2];
+      bv[0] = u0.x; bv[1] = u0.y; bv[2] = u1.x; bv[3] = u1.y;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fma(av[i], bv[j], acc[i][j]);
     }
-    P[i] = p;
+    __syncthreads();
+  }
+  const int bin = (n0 >> 1) + 2 * tx;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = m0 + ty * 8 + i;
+    if (r >= rows) break;
+    float2 p;
+    p.x = (float)fma(acc[i][0], acc[i][0], acc[i][1] * acc[i][1]);
+    p.y = (float)fma(acc[i][2], acc[i][2], acc[i][3] * acc[i][3]);
+    *(float2*)(P + (int64_t)r * FE_PK + bin) = p;
   }
 }
 
@@ -127,10 +186,10 @@ double mel_to_hz(double m) { return m < 15.0 ? 200.0 * m / 3.0 : 1000.0 * std::e
 struct aenc_frontend {
   aenc_frontend_config cfg{};
   int frames = 0;
-  float* dft = nullptr;       // [404, 400]
-  float* filters = nullptr;   // [n_mel, 208]
-  float* ws = nullptr;        // padded audio | X | P | mel | clip max
-  float *xp = nullptr, *X = nullptr, *P = nullptr, *mel = nullptr, *cmax = nullptr;
+  double* dft = nullptr;      // [448, 400]: row 2k cos, row 2k + 1 sin of bin k (rows past bin 200 zero)
+  float* filters = nullptr;   // [n_mel, 224]
+  float* ws = nullptr;        // padded audio | P | mel | clip max
+  float *xp = nullptr, *P = nullptr, *mel = nullptr, *cmax = nullptr;
 };
 
 namespace {
@@ -168,15 +227,16 @@ extern "C" aenc_frontend* aenc_frontend_create(const aenc_frontend_config* c) {
   h->cfg = *c;
   h->frames = (int)shape[2];
   const int B = c->batch, n_mel = c->n_mel;
-  // DFT rows: w[n] cos(2 pi k n / N) and w[n] sin(2 pi k n / N) (the sign of the
-  // imaginary part does not matter for the power).
-  std::vector<float> dft((size_t)FE_DFT_N * FE_NFFT, 0.0f);
+  // DFT rows: w[n] cos(2 pi k n / N) and w[n] sin(2 pi k n / N) of bin k at
+  // rows 2k and 2k + 1 (the sign of the imaginary part does not matter for
+  // the power).
+  std::vector<double> dft((size_t)FE_DFT_N * FE_NFFT, 0.0);
   for (int k = 0; k < FE_BINS; ++k)
     for (int n = 0; n < FE_NFFT; ++n) {
       const double w = 0.5 - 0.5 * std::cos(2.0 * M_PI * n / FE_NFFT);
       const double a = 2.0 * M_PI * (double)((int64_t)k * n % FE_NFFT) / FE_NFFT;
-      dft[(size_t)k * FE_NFFT + n] = (float)(w * std::cos(a));
-      dft[(size_t)(FE_BINS + k) * FE_NFFT + n] = (float)(w * std::sin(a));
+      dft[(size_t)(2 * k) * FE_NFFT + n] = w * std::cos(a);
+      dft[(size_t)(2 * k + 1) * FE_NFFT + n] = w * std::sin(a);
     }
   // Triangular filters between mel-spaced edges, each of unit area in Hz.
   std::vector<float> fb((size_t)n_mel * FE_PK, 0.0f);
@@ -192,12 +252,12 @@ extern "C" aenc_frontend* aenc_frontend_create(const aenc_frontend_config* c) {
       fb[(size_t)m * FE_PK + k] = (float)v;
     }
   const int64_t rows = (int64_t)B * h->frames;
-  const size_t n_xp = (size_t)B * (c->n_samples + FE_NFFT), n_X = (size_t)rows * FE_DFT_N, n_P = (size_t)rows * FE_PK,
+  const size_t n_xp = (size_t)B * (c->n_samples + FE_NFFT), n_P = (size_t)rows * FE_PK,
                n_mel_el = (size_t)rows * n_mel;
   hipError_t e;
-  if ((e = hipMalloc(&h->dft, dft.size() * 4)) != hipSuccess || (e = hipMalloc(&h->filters, fb.size() * 4)) != hipSuccess ||
-      (e = hipMalloc(&h->ws, (n_xp + n_X + n_P + n_mel_el + B + 64) * 4)) != hipSuccess ||
-      (e = hipMemcpy(h->dft, dft.data(), dft.size() * 4, hipMemcpyHostToDevice)) != hipSuccess ||
+  if ((e = hipMalloc(&h->dft, dft.size() * 8)) != hipSuccess || (e = hipMalloc(&h->filters, fb.size() * 4)) != hipSuccess ||
+      (e = hipMalloc(&h->ws, (n_xp + n_P + n_mel_el + B + 64) * 4)) != hipSuccess ||
+      (e = hipMemcpy(h->dft, dft.data(), dft.size() * 8, hipMemcpyHostToDevice)) != hipSuccess ||
       (e = hipMemcpy(h->filters, fb.data(), fb.size() * 4, hipMemcpyHostToDevice)) != hipSuccess) {
     fe_error(hipGetErrorString(e));
     fe_release(h);
@@ -205,8 +265,7 @@ extern "C" aenc_frontend* aenc_frontend_create(const aenc_frontend_config* c) {
     return nullptr;
   }
   h->xp = h->ws;
-  h->X = h->xp + n_xp;
-  h->P = h->X + n_X;
+  h->P = h->xp + n_xp;
   h->mel = h->P + n_P;
   h->cmax = h->mel + n_mel_el;
   return h;
@@ -226,13 +285,8 @@ extern "C" int aenc_frontend_run(aenc_frontend* h, const float* audio, void* mel
   hipLaunchKernelGGL(reflect_pad_kernel, dim3(2048), dim3(256), 0, s, audio, h->xp, n, B);
   if (!check(hipGetLastError())) return AENC_E_HIP;
   // frames: row r = b F + f starts at padded sample b (n + 400) + 160 f
-  EpiParams e1{};
-  e1.c = h->X;
-  e1.crow = dense_rows(FE_DFT_N);
-  if (!check(gemm_f32(EPI_STORE_F32, h->xp, RowMap{F, (int64_t)(n + FE_NFFT), FE_HOP, 0, nullptr}, h->dft, FE_NFFT,
-                      (int)rows, FE_DFT_N, FE_NFFT, nullptr, e1, s)))
-    return AENC_E_HIP;
-  hipLaunchKernelGGL(power_kernel, dim3(4096), dim3(256), 0, s, h->X, h->P, rows);
+  hipLaunchKernelGGL(dft_power_kernel, dim3(FE_DFT_N / DP_BN, (unsigned)((rows + DP_BM - 1) / DP_BM)), dim3(256), 0, s,
+                     h->xp, n + FE_NFFT, F, (int)rows, h->dft, h->P);
   if (!check(hipGetLastError())) return AENC_E_HIP;
   EpiParams e2{};
   e2.c = h->mel;

@@ -122,3 +122,14 @@ extern "C" int aenc_k_copy(void* dst, const void* src, int64_t bytes, void* stre
   if (!dst || !src || bytes <= 0 || bytes % 16) return fail("bad copy arguments");
   return hip_status(copy_bytes(dst, src, bytes, (hipStream_t)stream), "copy");
 }
+
+extern "C" int aenc_k_copy_stream(void* dst, const void* src, int64_t bytes, void* stream) {
+  if (!dst || !src || bytes <= 0 || bytes % 16) return fail("bad copy arguments");
+  if (!aligned16(dst) || !aligned16(src)) return fail("copy buffers must be 16-byte aligned");
+  return hip_status(copy_stream(dst, src, bytes, (hipStream_t)stream), "copy_stream");
+}
+
+extern "C" int aenc_k_mfma_loop(float* out, int blocks, int iters, void* stream) {
+  if (!out || blocks < 1 || iters < 1) return fail("mfma loop: need out, blocks >= 1 and iters >= 1");
+  return hip_status(mfma_loop(out, blocks, iters, (hipStream_t)stream), "mfma_loop");
+}

@@ -95,4 +95,11 @@ hipError_t gelu_f32(const float* x, float* y, int64_t n, hipStream_t stream);
 // Plain device copy kernel (16-byte vectors), for calibrating traffic counters.
 hipError_t copy_bytes(void* dst, const void* src, int64_t bytes, hipStream_t stream);
 
+// Calibration: a streaming copy with four 16-byte vectors in flight per lane
+// (the copy ceiling), and an MFMA loop on register operands, `blocks`
+// workgroups of 4 waves, each wave `iters` rounds of 4 independent
+// 32x32x16 bf16 MFMAs (the matrix-core ceiling); out holds blocks * 256 floats.
+hipError_t copy_stream(void* dst, const void* src, int64_t bytes, hipStream_t stream);
+hipError_t mfma_loop(float* out, int blocks, int iters, hipStream_t stream);
+
 }  // namespace aenc

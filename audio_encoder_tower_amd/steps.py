@@ -113,3 +113,17 @@ def copy(dst: torch.Tensor, src: torch.Tensor) -> None:
     nbytes = src.numel() * src.element_size()
     assert dst.numel() * dst.element_size() >= nbytes
     check(lib().aenc_k_copy(_p(dst), _p(src), nbytes, _s()), "aenc_k_copy")
+
+
+def copy_stream(dst: torch.Tensor, src: torch.Tensor) -> None:
+    """The streaming copy of the copy ceiling (aenc_k_copy_stream)."""
+    nbytes = src.numel() * src.element_size()
+    assert dst.numel() * dst.element_size() >= nbytes
+    check(lib().aenc_k_copy_stream(_p(dst), _p(src), nbytes, _s()), "aenc_k_copy_stream")
+
+
+def mfma_loop(out: torch.Tensor, blocks: int, iters: int) -> float:
+    """The matrix-core loop of the MFMA ceiling (aenc_k_mfma_loop); returns its FLOPs."""
+    assert out.dtype == torch.float32 and out.numel() >= blocks * 256
+    check(lib().aenc_k_mfma_loop(_p(out), blocks, iters, _s()), "aenc_k_mfma_loop")
+    return float(blocks) * 4 * iters * 4 * 32768

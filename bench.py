@@ -8,7 +8,12 @@ already resident in HBM. Prints one JSON line:
   tflops       algorithmic TFLOP/s, and mfma_frac = tflops / bf16 dense peak
   roofline     the kernel with the most time, against its own roofline, with
                its average launch time from HIP events on the forward's stream
-  cpu_baseline the fp64 CPU oracle on a bounded sample of the same workload
+  cpu_baseline the CPU oracle (float32 NumPy, every core of the process) on a
+               bounded sample of the same workload
+  ceilings     the part's own copy GB/s and bf16 MFMA-loop TFLOP/s
+  configs      the other workloads: batch-1 latency (eager and HIP-graph
+               replay), the variable-length batch on valid work, the stacked
+               projector and the chunked attention
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -31,7 +36,7 @@ METRIC = "encoder audio-seconds/sec (30 s chunks, bf16, 1 GPU) + % of bf16 MFMA 
 # MI355X published peaks: dense bf16 MFMA 2.5 PFLOP/s, fp32 157.3 TFLOP/s, HBM3E 8 TB/s.
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
-PEAK_F32_VALU_NOPK = 78.6   # fp32 vector FMA without packed math (packed math is off in this build)
+PEAK_F32_VALU_NOPK = 78.6   # fp32 (no packed math, off in this build) and fp64 vector FMA
 
 
 def step_flops(g, kind: str, rows: int, proj_rows: int) -> float:
@@ -54,40 +59,71 @@ def attention_flops(g, tb) -> float:
     return float(sum(4.0 * oracle.attended_pairs(int(t), g.attn_chunk, g.attn_chunk_mode) * g.d_model for t in tb))
 
 
-def cpu_baseline(w, blocks: int = 0):
-    """Time the oracle (as it is) on one clip: the stem, `blocks` of the blocks
-    (0: all of them) and the final norm (+ projector); block time is scaled to
-    the full depth when fewer blocks run."""
-    import oracle
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(w, blocks: int = 0, clips: int = 2):
+    """Time the oracle (as it is, in float32 with NumPy's BLAS on every core
+    this process may use) on `clips` clips of the workload: the stem, `blocks`
+    of the blocks (0: all of them) and the final norm (+ projector); block
+    time is scaled to the full depth when fewer blocks run."""
     from oracle import encoder as E
+    from threadpoolctl import threadpool_info, threadpool_limits
     g = w.geom
     blocks = g.n_layers if blocks <= 0 else min(blocks, g.n_layers)
     W = synth.make_weights(w.replace(geom=g.replace(n_layers=blocks)))
-    Wfull_proj = W
-    mel = synth.make_mel(w, clips=[0])[0]
-    mask = synth.make_mask(w, clips=[0])
-    m = None if mask is None else mask[0]
-    t0 = time.perf_counter()
-    x = E.stem(mel, W)
-    t1 = time.perf_counter()
-    x = E.blocks(x, W, blocks, g.n_heads, m, g.ln_eps)
-    t2 = time.perf_counter()
-    E.final(x, Wfull_proj, g.pool_step, g.ln_eps)
-    t3 = time.perf_counter()
-    per_clip = (t1 - t0) + (t2 - t1) * g.n_layers / blocks + (t3 - t2)
-    frames = synth.make_lengths(w, 1)[0]
+    clips = max(1, min(clips, g.batch))
+    mel = synth.make_mel(w, clips=list(range(clips)))
+    mask = synth.make_mask(w, clips=list(range(clips)))
     cores = len(os.sched_getaffinity(0))
+    t_stem = t_blocks = t_final = 0.0
+    with threadpool_limits(limits=cores, user_api="blas"):
+        blas = [{k: v for k, v in d.items() if k in ("internal_api", "version", "num_threads", "architecture",
+                                                    "threading_layer")}
+                for d in threadpool_info() if d.get("user_api") == "blas"]
+        for c in range(clips):
+            m = None if mask is None else mask[c]
+            t0 = time.perf_counter()
+            x = E.stem(mel[c], W, np.float32)
+            t1 = time.perf_counter()
+            x = E.blocks(x, W, blocks, g.n_heads, m, g.ln_eps, np.float32)
+            t2 = time.perf_counter()
+            E.final(x, W, g.pool_step, g.ln_eps, np.float32, g.stack)
+            t3 = time.perf_counter()
+            t_stem += t1 - t0
+            t_blocks += t2 - t1
+            t_final += t3 - t2
+    measured = t_stem + t_blocks + t_final
+    total = t_stem + t_blocks * g.n_layers / blocks + t_final
+    frames = float(synth.make_lengths(w, clips).sum())
     return {
-        "value": round(float(frames) / 100.0 / per_clip, 4),
+        "value": round(frames / 100.0 / total, 4),
         "unit": "audio-s/s",
         "cores": cores,
         "kind": "oracle",
-        "sample": (f"1 clip of {w.name}: stem + {blocks} of {g.n_layers} blocks + final norm"
-                   f"{' + projector' if g.proj_hidden else ''}, fp64 NumPy"
+        "sample": (f"{clips} clip(s) of {w.name}: stem + {blocks} of {g.n_layers} blocks + final norm"
+                   f"{' + projector' if g.proj_hidden else ''}, float32 NumPy"
                    f"{'' if blocks == g.n_layers else f'; block time scaled x{g.n_layers / blocks:g}'}; "
-                   f"measured {t3 - t0:.1f} s"),
-        "seconds_per_clip": round(per_clip, 3),
+                   f"measured {measured:.1f} s"),
+        "seconds_per_clip": round(total / clips, 3),
+        "tflops": round(oracle_flops(w, clips) / total / 1e12, 4),
+        "cpu_model": _cpu_model(),
+        "blas": blas,
     }
+
+
+def oracle_flops(w, clips: int) -> float:
+    import oracle  # closed-form FLOP count only
+    return oracle.flops(w.geom.replace(batch=clips), synth.make_lengths(w, clips))
 
 
 # Kernel sources whose change invalidates stored hardware-counter readings.
@@ -141,15 +177,176 @@ def frontend_leg(batch: int, steps: int):
     ms = start.elapsed_time(end) / steps
     fe.close()
     frames = batch * (n // 160)
-    dft_flops = 2.0 * frames * 404 * 400
-    mel_flops = 2.0 * frames * 128 * 208
+    # algorithmic work: real and imaginary parts of bins 0..200 over 400
+    # samples (fp64), then 128 filters over the 201 bins (fp32)
+    dft_flops = 2.0 * frames * 402 * 400
+    mel_flops = 2.0 * frames * 128 * 201
     tf = (dft_flops + mel_flops) / (ms * 1e-3) / 1e12
     return {"workload": f"{batch} clips of 30 s, 16 kHz -> [{batch}, 128, 3000] bf16", "ms_per_batch": round(ms, 4),
             "audio_s_per_s": round(batch * 30.0 / (ms * 1e-3), 1),
-            "fp32_tflops": round(tf, 2),
-            # fp32 GEMMs on the vector ALUs without packed math: 256 CUs x 64 lanes x 2 FLOP x 2.4 GHz
+            "tflops": round(tf, 2), "dft_fp64_gflop": round(dft_flops / 1e9, 2),
+            # fp64 and fp32 FMA on the vector ALUs at the same full rate (no packed
+            # math): 256 CUs x 64 lanes x 2 FLOP x 2.4 GHz
             "roofline": {"bound": "alu", "achieved": round(tf, 2), "peak": PEAK_F32_VALU_NOPK, "unit": "TFLOP/s",
                          "frac": round(tf / PEAK_F32_VALU_NOPK, 4)}}
+
+
+def ceilings_leg(reps: int = 10):
+    """The part's own ceilings, measured with the library's calibration
+    kernels: a 1 GiB streaming copy (read + write bytes per second) and the
+    bf16 MFMA loop on register operands (no memory traffic)."""
+    import torch
+    import audio_encoder_tower_amd as aenc
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, n):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(n):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    nbytes = 1 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    src.random_(0, 256)
+    dst = torch.empty_like(src)
+    ms_copy = timed(lambda: aenc.steps.copy_stream(dst, src), reps)
+    ms_plain = timed(lambda: aenc.steps.copy(dst, src), reps)
+    assert torch.equal(dst, src)
+    del src, dst
+    blocks, iters = 4096, 2048
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    flops = blocks * 4.0 * iters * 4 * 32768
+    ms_mfma = timed(lambda: aenc.steps.mfma_loop(out, blocks, iters), reps)
+    assert bool(torch.isfinite(out).all())
+    return {
+        "copy_gbs": round(2 * nbytes / (ms_copy * 1e-3) / 1e9, 1),
+        "copy_frac_of_8tbs": round(2 * nbytes / (ms_copy * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "copy_plain_gbs": round(2 * nbytes / (ms_plain * 1e-3) / 1e9, 1),
+        "copy_bytes": 2 * nbytes,
+        "mfma_bf16_tflops": round(flops / (ms_mfma * 1e-3) / 1e12, 1),
+        "mfma_frac_of_peak": round(flops / (ms_mfma * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"], 4),
+        "mfma_loop": f"{blocks} workgroups x 4 waves x {iters} rounds x 4 chains of 32x32x16 bf16 MFMAs",
+    }
+
+
+# Workloads timed beside the headline: batch-1 latency (with HIP-graph replay),
+# the variable-length batch on valid work only, the stacked projector and the
+# chunked attention.
+CONFIG_LEGS = ["whisper_large_b1", "whisper_large_varlen_b32", "whisper_large_stack4_proj_b16", "tiny_fp32_b1",
+               "whisper_medium_pool2_b1", "whisper_medium_pool2_chunk1s_b16"]
+
+
+def time_forwards(enc, mel, mask, out, steps: int, warmup: int, stream):
+    import torch
+    for _ in range(warmup):
+        enc.forward(mel, mask, out, stream)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        enc.forward(mel, mask, out, stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def time_graph_replays(enc, mel, mask, out, steps: int):
+    """One forward captured into a HIP graph, then `steps` replays."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        enc.forward(mel, mask, out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        enc.forward(mel, mask, out)
+    graph.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        graph.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    del graph
+    return a.elapsed_time(b) / steps
+
+
+def device_weights(w, cache: dict, tdt):
+    """Device copies of the workload's weights, reusing the encoder part and
+    the projector part across workloads that share their seeds and shapes
+    (each tensor has its own seeded stream, so the values are the same)."""
+    import torch
+    g = w.geom
+    enc_key = ("enc", w.weight_seed, w.init, g.dtype, g.n_mel, g.d_model, g.n_layers, g.d_ffn)
+    proj_key = ("proj", w.proj_seed, w.init, g.dtype, g.proj_in, g.proj_hidden, g.proj_out)
+    for k in [k for k in cache if k not in (enc_key, proj_key)]:
+        del cache[k]
+    if enc_key not in cache:
+        W = synth.make_weights(w.replace(geom=g.replace(proj_hidden=0, proj_out=0, stack=1)))
+        cache[enc_key] = {k: torch.from_numpy(v).to("cuda").to(tdt) for k, v in W.items()}
+    out = dict(cache[enc_key])
+    if g.proj_hidden:
+        if proj_key not in cache:
+            # projector tensors draw from their own seed: the same values whatever the depth
+            W = synth.make_weights(w.replace(geom=g.replace(n_layers=0)))
+            cache[proj_key] = {k: torch.from_numpy(v).to("cuda").to(tdt) for k, v in W.items()
+                               if k.startswith("proj")}
+        out.update(cache[proj_key])
+    return out
+
+
+def configs_leg(names, steps: int, warmup: int, weights_cache: dict):
+    """Each workload in `names` timed like the headline (inputs resident in
+    HBM, HIP events on the forward's stream). Batch-1 workloads also report
+    HIP-graph replay of the same forward."""
+    import torch
+    import audio_encoder_tower_amd as aenc
+    import oracle  # closed-form FLOP count only
+    out_rec = {}
+    stream = torch.cuda.current_stream()
+    for name in names:
+        w = synth.get_workload(name)
+        g = w.geom
+        tdt = torch.bfloat16 if g.dtype == "bf16" else torch.float32
+        enc = aenc.Encoder(g, device_weights(w, weights_cache, tdt))
+        mel = torch.from_numpy(synth.make_mel(w)).to("cuda").to(tdt)
+        mask_np = synth.make_mask(w)
+        mask = None if mask_np is None else torch.from_numpy(mask_np).to("cuda")
+        out = torch.empty(enc.out_shape, dtype=enc.out_dtype, device="cuda")
+        n = steps if g.batch > 1 else 5 * steps
+        ms = time_forwards(enc, mel, mask, out, n, warmup, stream)
+        frames = synth.make_lengths(w)
+        fl = oracle.flops(g, frames)
+        audio_s = float(frames.sum()) / 100.0
+        peak = PEAK_TFLOPS[g.dtype]
+        rec = {"batch": g.batch, "dtype": g.dtype, "ms_per_forward": round(ms, 4),
+               "audio_s_per_s": round(audio_s / (ms * 1e-3), 1), "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
+               "frac_of_peak": round(fl / (ms * 1e-3) / 1e12 / peak, 4), "flops_per_forward": fl,
+               "audio_s_per_forward": audio_s}
+        if w.varlen:
+            rec["valid_frames"] = int(frames.sum())
+            rec["padded_frames"] = int(g.batch * g.n_frames)
+            rec["counted"] = "valid positions and key pairs only"
+        if g.batch == 1:
+            gms = time_graph_replays(enc, mel, mask, out, n)
+            rec["graph_ms_per_forward"] = round(gms, 4)
+            rec["graph_audio_s_per_s"] = round(audio_s / (gms * 1e-3), 1)
+        enc.close()
+        del mel, mask, out
+        out_rec[name] = rec
+        print(f"config {name}: {rec}", file=sys.stderr, flush=True)
+    weights_cache.clear()
+    torch.cuda.empty_cache()
+    return out_rec
 
 
 def cache_leg(enc, mel, mask, out, audio_s: float, steps: int):
@@ -279,6 +476,10 @@ def main():
                     help="skip the encoder-beside-decode overlap measurement")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run the plain copy kernel over this many MiB (a reference for traffic counters)")
+    ap.add_argument("--cpu-clips", type=int, default=2, help="clips the CPU oracle encodes")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip timing the other workloads (batch-1 latency, variable length, stacked, chunked)")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the copy and MFMA-loop ceilings")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -295,9 +496,8 @@ def main():
     torch.cuda.set_device(dev)
     tdt = torch.bfloat16 if g.dtype == "bf16" else torch.float32
 
-    W = synth.make_weights(w)
-    enc = aenc.Encoder(g, {k: torch.from_numpy(v).to(dev).to(tdt) for k, v in W.items()})
-    del W
+    weights_cache = {}
+    enc = aenc.Encoder(g, device_weights(w, weights_cache, tdt))
     mel = torch.from_numpy(synth.make_mel(w)).to(dev).to(tdt)
     mask_np = synth.make_mask(w)
     mask = None if mask_np is None else torch.from_numpy(mask_np).to(dev)
@@ -400,15 +600,29 @@ def main():
         "roofline": roofline,
         "kernels": per_kind,
     }
+    print(f"headline {w.name}: {ms_step:.3f} ms per forward", file=sys.stderr, flush=True)
     if not args.no_frontend:
         result["frontend"] = frontend_leg(g.batch, args.steps)
     if not args.no_side_stream:
         result["side_stream"] = side_stream_leg(enc, mel, mask, out, audio_s)
         result["cache"] = cache_leg(enc, mel, mask, out, audio_s, args.steps)
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_blocks)
-    print(json.dumps(result), flush=True)
     enc.close()
+    if not args.no_ceilings:
+        c = ceilings_leg()
+        result["ceilings"] = c
+        # the same kernels against the part's own ceilings
+        roofline["frac_of_measured_ceiling"] = round(roofline["achieved"] / c["mfma_bf16_tflops"], 4)
+        result["mfma_frac_of_measured_ceiling"] = round(tflops / c["mfma_bf16_tflops"], 4)
+        if "layernorm" in per_kind:
+            per_kind["layernorm"]["frac_of_copy_ceiling"] = round(per_kind["layernorm"]["gbs"] / c["copy_gbs"], 4)
+        print(f"ceilings: {c}", file=sys.stderr, flush=True)
+    if not args.no_configs:
+        result["configs"] = configs_leg([n for n in CONFIG_LEGS if n != w.name], args.steps, args.warmup,
+                                        weights_cache)
+    weights_cache.clear()
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_blocks, args.cpu_clips)
+    print(json.dumps(result), flush=True)
 
 
 if __name__ == "__main__":

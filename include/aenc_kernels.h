@@ -102,6 +102,19 @@ int aenc_k_row_maps(const uint8_t *mask, int B, int T, int32_t *row_map, int32_t
  * reference point for hardware traffic counters. */
 int aenc_k_copy(void *dst, const void *src, int64_t bytes, void *stream);
 
+/* Ceilings of this part, measured beside the published peaks (the encoder's
+ * kernels are reported against both). Neither is a step of the encoder.
+ * aenc_k_copy_stream: dst = src, `bytes` (a multiple of 16; both 16-byte
+ * aligned), four 16-byte vectors in flight per lane: the read+write rate a
+ * plain streaming kernel reaches.
+ * aenc_k_mfma_loop: `blocks` workgroups of 4 waves; each wave runs `iters`
+ * rounds of 4 independent v_mfma_f32_32x32x16_bf16 (32768 FLOP each) on
+ * register operands with varied non-zero bf16 values, and writes one sum per
+ * lane to out (fp32, blocks * 256 elements): the bf16 matrix-core rate with
+ * no memory traffic. FLOPs per launch = blocks * 4 * iters * 4 * 32768. */
+int aenc_k_copy_stream(void *dst, const void *src, int64_t bytes, void *stream);
+int aenc_k_mfma_loop(float *out, int blocks, int iters, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -30,6 +30,15 @@ def main(names):
             every = parity.FULL_SIZE_SAMPLES[name]["every"]
             res = parity.oracle_clip(w, clip, W, every=every)
             print(f"{name} clip {clip}: {res['out'].shape} in {time.time() - t0:.1f} s", flush=True)
+    for name, clips in parity.EXTRA_CLIPS.items():
+        if names and name not in names:
+            continue
+        w = synth.get_workload(name)
+        W = synth.make_weights(w)
+        for clip in clips:
+            t0 = time.time()
+            res = parity.oracle_clip(w, clip, W, every=1)
+            print(f"{name} clip {clip}: {res['out'].shape} in {time.time() - t0:.1f} s", flush=True)
 
 
 if __name__ == "__main__":

@@ -54,23 +54,40 @@ def assert_f32_parity(got, ref, what=""):
 # Oracle outputs, cached per (workload, clip, rows) and keyed on the oracle's source.
 # ---------------------------------------------------------------------------
 
+def _digest():
+    """A fast digest over whole byte buffers (xxh3 when the xxhash package is
+    present, else SHA-256)."""
+    try:
+        import xxhash
+        return xxhash.xxh3_128()
+    except ImportError:
+        return hashlib.sha256()
+
+
 def _fingerprint(W: dict, mel: np.ndarray, mask) -> str:
-    """Digest of the inputs the oracle reads (strided samples of every tensor)."""
-    h = hashlib.sha256()
+    """Digest of every byte the oracle reads: all weight tensors in full, the
+    mel input and the mask."""
+    h = _digest()
     for name in sorted(W):
-        a = np.ascontiguousarray(W[name], np.float32).ravel()
         h.update(name.encode() + str(W[name].shape).encode())
-        h.update(a[:: max(1, a.size // 4096)].tobytes())
-    h.update(np.ascontiguousarray(mel, np.float32).tobytes())
+        h.update(np.ascontiguousarray(W[name], np.float32).data)
+    h.update(np.ascontiguousarray(mel, np.float32).data)
     if mask is not None:
-        h.update(np.ascontiguousarray(mask).tobytes())
+        h.update(np.ascontiguousarray(mask).data)
+    return h.hexdigest()
+
+
+def _sources_digest() -> str:
+    """The oracle's source and the seeded input generators' source."""
+    h = hashlib.sha256()
+    for mod in (oracle.encoder, synth.inputs, synth.workloads):
+        h.update(inspect.getsource(mod).encode())
     return h.hexdigest()
 
 
 def _key(w: synth.Workload, clip: int, W: dict, mel: np.ndarray, mask) -> str:
     spec = json.dumps({"geom": repr(w.geom), "clip": clip, "data": _fingerprint(W, mel, mask),
-                       "oracle": hashlib.sha256(inspect.getsource(oracle.encoder).encode()).hexdigest()},
-                      sort_keys=True)
+                       "sources": _sources_digest()}, sort_keys=True)
     return hashlib.sha256(spec.encode()).hexdigest()[:24]
 
 
@@ -84,8 +101,9 @@ def oracle_clip(w: synth.Workload, clip: int, W: Optional[dict] = None, every: i
     """Oracle output of one clip: {"rows": indices, "out": [len(rows), D_out]} (fp64).
 
     The clip runs alone (clips are independent) with its own mask row. The
-    cache key covers the geometry, a digest of the weights and inputs and the
-    oracle's source, so a stale entry is never read.
+    cache key covers the geometry, a digest of every weight and input byte,
+    and the source of the oracle and of the input generators, so a stale
+    entry is never read.
     """
     if W is None:
         W = synth.make_weights(w)
@@ -111,11 +129,16 @@ FULL_SIZE_SAMPLES = {
     "tiny_fp32_b1": dict(clips=[0], every=1),
     "whisper_medium_pool2_b1": dict(clips=[0], every=1),
     "whisper_large_b1": dict(clips=[0], every=1),
-    "whisper_large_proj_b16": dict(clips=[0, 15], every=5),
+    "whisper_large_proj_b16": dict(clips=[0, 7, 15], every=5),
     "whisper_large_stack4_proj_b16": dict(clips=[0, 15], every=3),
     "whisper_large_varlen_b32": dict(clips=None, every=5),   # shortest, longest and one in between
     "whisper_medium_pool2_chunk1s_b16": dict(clips=[0, 15], every=3),
 }
+
+
+# Further oracle outputs the GPU tests read (whole clips): the distinct mels of
+# the last two clips of the largest-batch test.
+EXTRA_CLIPS = {"whisper_large_b1": [1, 2]}
 
 
 def varlen_sample_clips(w: synth.Workload) -> Sequence[int]:

@@ -158,6 +158,9 @@ def test_null_arguments(aenc):
     assert L.aenc_output_shape(ctypes.byref(g), None) == -1
     assert L.aenc_k_gemm_bf16(0, None, 0, None, None, None, 0, 1, 1, 64, -1, None) == -1
     assert L.aenc_k_copy(None, None, 16, None) == -1
+    assert L.aenc_k_copy_stream(None, None, 16, None) == -1
+    assert L.aenc_k_mfma_loop(None, 1, 1, None) == -1
+    assert L.aenc_k_mfma_loop(ctypes.c_void_p(16), 0, 1, None) == -1
     # kernel entry points reject bad sizes before any launch
     buf = ctypes.c_void_p(16)
     assert L.aenc_k_gemm_bf16(0, buf, 64, buf, None, buf, 64, 64, 64, 100, -1, None) == -1

@@ -3,7 +3,9 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import synth
+from tests import parity
 
 pytestmark = pytest.mark.gpu
 
@@ -60,30 +62,46 @@ def test_copies_are_ordered_across_streams(aenc):
 
 
 def test_forward_cached(aenc):
+    """Cache hits are the forward's output bit for bit, and both meet the bf16
+    bar against the oracle: the first batch (all misses), the all-hit batch,
+    and a batch with one new clip (run by the forward, stored alone)."""
     w = synth.get_workload("whisper_large_b1")
     w = w.replace(geom=w.geom.replace(batch=3, n_layers=1, n_frames=400), init="perturbed")
     g = w.geom
     W = synth.make_weights(w)
     enc = aenc.Encoder(g, {k: torch.from_numpy(v).to(DEV).to(torch.bfloat16) for k, v in W.items()})
-    mel = torch.from_numpy(synth.make_mel(w)).to(DEV).to(torch.bfloat16)
+    mel_np = synth.make_mel(w)
+    mel = torch.from_numpy(mel_np).to(DEV).to(torch.bfloat16)
     ref = enc.forward(mel).clone()
+    want = oracle.encode(g, W, mel_np)
     cache = aenc.EmbeddingsCache.for_encoder(enc, 8)
     out, hits = enc.forward_cached(cache, [10, 11, 12], mel)
     torch.cuda.synchronize()
     assert hits == 0 and torch.equal(out, ref)
+    parity.assert_bf16_parity(out.double().cpu().numpy(), want, "cached forward, all misses")
     enc.profile(True)
     out2, hits2 = enc.forward_cached(cache, [10, 11, 12], mel)
     torch.cuda.synchronize()
     stats = enc.profile_read()
     assert hits2 == 3 and torch.equal(out2, ref)
     assert sum(n for _, n in stats.values()) == 0      # served by copies: no kernel launched
+    m = parity.assert_bf16_parity(out2.double().cpu().numpy(), want, "cached forward, all hits")
+    print("all hits vs oracle", m)
     # a batch with one new clip runs the forward and stores only the new clip
-    mel2 = mel.clone()
-    mel2[1] = torch.from_numpy(synth.make_mel(w.replace(mel_seed=9), clips=[1])[0]).to(DEV).to(torch.bfloat16)
+    mel2_np = mel_np.copy()
+    mel2_np[1] = synth.make_mel(w.replace(mel_seed=9), clips=[1])[0]
+    mel2 = torch.from_numpy(mel2_np).to(DEV).to(torch.bfloat16)
     ref2 = enc.forward(mel2).clone()
     out3, hits3 = enc.forward_cached(cache, [10, 99, 12], mel2)
     torch.cuda.synchronize()
     assert hits3 == 2 and torch.equal(out3, ref2)
+    want2 = oracle.encode(g, W, mel2_np)
+    parity.assert_bf16_parity(out3.double().cpu().numpy(), want2, "cached forward, one new clip")
+    # the new clip is now served from the cache
+    out4, hits4 = enc.forward_cached(cache, [99, 10, 12], mel2[[1, 0, 2]].contiguous())
+    torch.cuda.synchronize()
+    assert hits4 == 3
+    parity.assert_bf16_parity(out4.double().cpu().numpy(), want2[[1, 0, 2]], "cached forward, stored new clip")
     s = cache.stats()
     assert s["entries"] == 4 and s["inserts"] == 4
     enc.profile(False)

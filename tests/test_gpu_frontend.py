@@ -33,10 +33,14 @@ def test_frontend_matches_the_oracle(aenc, n_samples, n_mel, clips):
     ref = FE.log_mel_batch(audio.astype(np.float64), n_mel)
     assert got.shape == ref.shape == (clips, n_mel, n_samples // 160)
     err = np.abs(got - ref)
-    # fp32 DFT and filter sums against fp64: spectral valleys just above the
-    # 80 dB floor carry the largest relative error (about 1e-3 in power)
-    assert err.max() <= 1e-3, err.max()
-    assert np.median(err) <= 1e-5, np.median(err)
+    from tests import parity
+    m = parity.assert_f32_parity(got.reshape(-1, got.shape[-1]), ref.reshape(-1, ref.shape[-1]),
+                                 f"frontend {n_samples}/{n_mel}")
+    print(f"frontend {n_samples}/{n_mel}: max-abs {err.max():.3e}, median {np.median(err):.3e}, "
+          f"normwise max-rel {m['max_rel']:.3e}", flush=True)
+    # fp64 DFT sums: every feature within 1e-4 of the fp64 oracle, not only
+    # relative to the largest one
+    assert err.max() <= 1e-4, err.max()
 
 
 def test_frontend_bf16_output_is_the_rounded_features(aenc):

@@ -75,7 +75,7 @@ REDUCED = {
     # full-width variable-length batch, one block
     "varlen_large_1block": reduced("whisper_large_varlen_b32", "varlen_large_1block",
                                    dict(batch=4, n_layers=1)),
-    # sharp attention (Q and K weights std 0.2)
+    # sharp attention (Q and K weights std 0.05: scores of std ~3)
     "sharp_attention": reduced("whisper_large_b1", "sharp_attention",
                                dict(n_layers=2, n_frames=600), init="sharp"),
     # no blocks: stem, positions and final LayerNorm only
@@ -226,28 +226,33 @@ def test_deterministic_and_batch_independent(aenc):
 def test_forward_at_the_bf16_batch_limit(aenc):
     """The largest Whisper-large bf16 batch that validation accepts (278
     clips): the FFN hidden rows then span 4,281,466,880 bytes, so the GEMM
-    copies of the last clips use buffer offsets above 2^31. The same clip is
-    repeated; every copy of it must come out bit-identical to the first and
-    match the oracle."""
+    copies of the last clips use buffer offsets above 2^31. Clips 0..275 hold
+    one mel (stream 0) and must come out bit-identical to each other; the last
+    two clips hold mels of their own (streams 1 and 2), so that a wrong offset
+    above 2^31 that read another clip's rows could not pass, and each is
+    checked against its own oracle output."""
     w = synth.get_workload("whisper_large_b1")
     W = synth.make_weights(w)
     g = w.geom.replace(batch=278)
     assert aenc.validate(g) == 0 and aenc.validate(g.replace(batch=279)) == -1
     print(f"gpu forward whisper_large_b1 x 278 geom={g}", flush=True)
     enc = aenc.Encoder(g, device_weights(W, g.dtype))
-    mel1 = torch.from_numpy(synth.make_mel(w)).to(DEV).to(torch.bfloat16)
-    mel = mel1.expand(g.batch, -1, -1).contiguous()
+    mels = torch.from_numpy(synth.make_mel(w, clips=[0, 1, 2])).to(DEV).to(torch.bfloat16)
+    mel = mels[0:1].expand(g.batch, -1, -1).contiguous()
+    mel[276] = mels[1]
+    mel[277] = mels[2]
     out = enc.forward(mel)
     torch.cuda.synchronize()
-    picks = [0, 139, 276, 277]
+    picks = [0, 139, 275, 276, 277]
     got = out[picks].float().cpu().numpy().astype(np.float64)
     del out, mel
     enc.close()
-    for i in range(1, len(picks)):
+    for i in (1, 2):
         np.testing.assert_array_equal(got[i], got[0], err_msg=f"clip {picks[i]} differs from clip 0")
-    ref = parity.oracle_clip(w, 0, W, every=1)
-    m = parity.assert_bf16_parity(got[-1][ref["rows"]], ref["out"], "batch 278, clip 277")
-    print("batch limit", m, flush=True)
+    for i, stream in ((0, 0), (3, 1), (4, 2)):
+        ref = parity.oracle_clip(w, stream, W, every=1)
+        m = parity.assert_bf16_parity(got[i][ref["rows"]], ref["out"], f"batch 278, clip {picks[i]}")
+        print(f"batch limit clip {picks[i]} (mel stream {stream})", m, flush=True)
 
 
 def test_padded_frames_do_not_change_valid_rows(aenc):
