@@ -54,14 +54,10 @@ struct GemmArgs {
   const bf16_t* W;
   int64_t ldw;
   int M, N, K;
-  const int32_t* m_dev;  // if set, M = *m_dev (rows beyond it are not computed)
+  const int32_t* m_dev;  // if set, M = min(*m_dev, M) (rows beyond it are not computed)
   uint32_t a_bytes, w_bytes;   // extents of A and W reachable through the row maps
-  int tiles_m, tiles_n, grid;
+  int tiles_n;
   EpiParams epi;
-  // 256x256 kernel with a split tail: each XCD takes tiles_per_xcd tiles,
-  // runs the first split_full whole and the rest as two 256x128 halves
-  // (split_full = 0: no split, grid / N_XCD whole tiles per XCD)
-  int tiles_per_xcd, split_full;
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -116,43 +112,45 @@ __device__ __forceinline__ void mma(f32x16 (&acc)[SM][SN], const bf16x8 (&fa)[SM
     for (int j = 0; j < SN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
 }
 
-// Tile index (XCD-contiguous) -> (tm, tn): GROUP_M-tall groups walked column
-// by column.
-__device__ __forceinline__ void tile_group_order(const GemmArgs& g, int tile, int& tm, int& tn) {
-  const int group_size = GEMM_GROUP_M * g.tiles_n;
+// Tile index -> (tm, tn): GROUP_M-tall groups walked column by column.
+__device__ __forceinline__ void tile_group_order(int tiles_m, int tiles_n, int tile, int& tm, int& tn) {
+  const int group_size = GEMM_GROUP_M * tiles_n;
   const int group = tile / group_size;
   const int first_m = group * GEMM_GROUP_M;
-  const int gm = min(g.tiles_m - first_m, GEMM_GROUP_M);
+  const int gm = min(tiles_m - first_m, GEMM_GROUP_M);
   const int in_group = tile - group * group_size;
   tm = first_m + in_group % gm;
   tn = in_group / gm;
 }
 
-// Tile (tm, tn) of workgroup blockIdx.x: XCD-contiguous ranges of tiles, in
-// group order. False for padding workgroups.
-__device__ __forceinline__ bool tile_of_block(const GemmArgs& g, int& tm, int& tn) {
-  const int per_xcd = g.grid / N_XCD;
-  const int tile = (blockIdx.x % N_XCD) * per_xcd + blockIdx.x / N_XCD;
-  if (tile >= g.tiles_m * g.tiles_n) return false;
-  tile_group_order(g, tile, tm, tn);
-  return true;
-}
-
-// The same for the 256x256 kernel, whose tail may be split: half is -1 for a
-// whole tile, else which 128-column half of tile (tm, tn) the workgroup
-// takes. When an XCD's tiles leave a last round of at most 16 on its 32 CUs,
-// halving those tiles spreads that round over twice as many CUs.
-__device__ __forceinline__ bool big_tile_of_block(const GemmArgs& g, int& tm, int& tn, int& half) {
-  half = -1;
-  if (g.split_full == 0) return tile_of_block(g, tm, tn);
+// Tile (tm, tn) of workgroup blockIdx.x for an M-row product (M read on the
+// device, so a launch sized for the longest batch balances the rows a masked
+// batch really has): the tiles are split into 8 contiguous ranges, one per XCD
+// (workgroup b runs on XCD b mod 8), of total/8 or total/8 + 1 tiles, walked in
+// group order. With SPLIT, when an XCD's range leaves a last round of at most
+// 16 tiles on its 32 CUs, those tiles run as two 128-column halves each
+// (`half` 0 or 1; -1 for a whole tile). False for workgroups past the work.
+template <bool SPLIT>
+__device__ __forceinline__ bool tile_of_block(const GemmArgs& g, int M, int BM, int& tm, int& tn, int& half) {
+  const int tiles_m = (M + BM - 1) / BM;
+  const int total = tiles_m * g.tiles_n;
   const int x = blockIdx.x % N_XCD, i = blockIdx.x / N_XCD;
-  int tile = x * g.tiles_per_xcd + i;
-  if (i >= g.split_full) {
-    tile = x * g.tiles_per_xcd + g.split_full + (i - g.split_full) / 2;
-    half = (i - g.split_full) & 1;
+  const int base = total / N_XCD, rem = total % N_XCD;
+  const int cnt = base + (x < rem ? 1 : 0), first = x * base + min(x, rem);
+  int full = cnt;
+  if (SPLIT) {
+    const int tail = cnt % CUS_PER_XCD;
+    if (cnt > CUS_PER_XCD && tail > 0 && 2 * tail <= CUS_PER_XCD) full = cnt - tail;
   }
-  if (tile >= g.tiles_m * g.tiles_n) return false;
-  tile_group_order(g, tile, tm, tn);
+  int t = i;
+  half = -1;
+  if (i >= full) {
+    if (i >= full + 2 * (cnt - full)) return false;
+    t = full + (i - full) / 2;
+    half = (i - full) & 1;
+  }
+  if (t >= cnt) return false;
+  tile_group_order(tiles_m, g.tiles_n, first + t, tm, tn);
   return true;
 }
 
@@ -365,11 +363,10 @@ __global__ __launch_bounds__(SMALL_THREADS) void gemm_bf16_128_kernel(GemmArgs g
   __shared__ __attribute__((aligned(16))) bf16_t buf0[(BM + BN) * GEMM_BK];
   __shared__ __attribute__((aligned(16))) bf16_t buf1[(BM + BN) * GEMM_BK];
 
-  int tm, tn;
-  if (!tile_of_block(g, tm, tn)) return;
-  const int M = g.m_dev ? *g.m_dev : g.M;
+  const int M = g.m_dev ? min(*g.m_dev, g.M) : g.M;
+  int tm, tn, half;
+  if (!tile_of_block<false>(g, M, BM, tm, tn, half)) return;
   const int m0 = tm * BM, n0 = tn * BN;
-  if (m0 >= M) return;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -681,11 +678,10 @@ __global__ __launch_bounds__(BIG_THREADS) void gemm_bf16_256_kernel(GemmArgs g) 
   __shared__ __attribute__((aligned(16))) bf16_t lw0[BN * GEMM_BK];
   __shared__ __attribute__((aligned(16))) bf16_t lw1[BN * GEMM_BK];
 
-  int tm, tn, half = -1;
-  if (!(SPLIT ? big_tile_of_block(g, tm, tn, half) : tile_of_block(g, tm, tn))) return;
-  const int M = g.m_dev ? *g.m_dev : g.M;
+  const int M = g.m_dev ? min(*g.m_dev, g.M) : g.M;
+  int tm, tn, half;
+  if (!tile_of_block<SPLIT>(g, M, BM, tm, tn, half)) return;
   const int m0 = tm * BM, n0 = tn * BN;
-  if (m0 >= M) return;
   if (!SPLIT || half < 0) {
     big_tile<EPI, 4>(g, m0, n0, M, la0, la1, la2, lw0, lw1);
   } else {
@@ -697,30 +693,32 @@ __global__ __launch_bounds__(BIG_THREADS) void gemm_bf16_256_kernel(GemmArgs g) 
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
+// Whether some XCD's tile range leaves a last round that the split tail halves
+// (the same rule as tile_of_block<true>, for the host's row count).
+static bool split_pays(int total) {
+  for (int x = 0; x < N_XCD; ++x) {
+    const int cnt = total / N_XCD + (x < total % N_XCD ? 1 : 0), tail = cnt % CUS_PER_XCD;
+    if (cnt > CUS_PER_XCD && tail > 0 && 2 * tail <= CUS_PER_XCD) return true;
+  }
+  return false;
+}
+
 template <int EPI>
 static hipError_t launch_epi(GemmArgs g, int tile_cfg, hipStream_t stream) {
   const int bt = tile_cfg == GEMM_TILE_256x256 ? 256 : 128;
-  g.tiles_m = (g.M + bt - 1) / bt;
   g.tiles_n = (g.N + bt - 1) / bt;
-  const int total = g.tiles_m * g.tiles_n;
-  g.grid = (total + N_XCD - 1) / N_XCD * N_XCD;
-  g.tiles_per_xcd = 0;
-  g.split_full = 0;
-  if (tile_cfg == GEMM_TILE_256x256 && total % N_XCD == 0) {
-    // a last round of at most half the XCD's CUs runs as half tiles
-    const int per = total / N_XCD, tail = per % CUS_PER_XCD;
-    if (per > CUS_PER_XCD && tail > 0 && 2 * tail <= CUS_PER_XCD) {
-      g.tiles_per_xcd = per;
-      g.split_full = per - tail;
-      g.grid = N_XCD * (per + tail);
-    }
+  // sized for g.M rows; a device row count below it leaves workgroups idle
+  const int total = (g.M + bt - 1) / bt * g.tiles_n;
+  const int per_xcd = (total + N_XCD - 1) / N_XCD;
+  if (tile_cfg == GEMM_TILE_256x256 && split_pays(total)) {
+    // a split XCD runs at most 16 extra half-tile workgroups
+    hipLaunchKernelGGL((gemm_bf16_256_kernel<EPI, true>), dim3(N_XCD * (per_xcd + CUS_PER_XCD / 2)),
+                       dim3(BIG_THREADS), 0, stream, g);
+  } else if (tile_cfg == GEMM_TILE_256x256) {
+    hipLaunchKernelGGL((gemm_bf16_256_kernel<EPI, false>), dim3(N_XCD * per_xcd), dim3(BIG_THREADS), 0, stream, g);
+  } else {
+    hipLaunchKernelGGL((gemm_bf16_128_kernel<EPI>), dim3(N_XCD * per_xcd), dim3(SMALL_THREADS), 0, stream, g);
   }
-  if (tile_cfg == GEMM_TILE_256x256 && g.split_full == 0)
-    hipLaunchKernelGGL((gemm_bf16_256_kernel<EPI, false>), dim3(g.grid), dim3(BIG_THREADS), 0, stream, g);
-  else if (tile_cfg == GEMM_TILE_256x256)
-    hipLaunchKernelGGL((gemm_bf16_256_kernel<EPI, true>), dim3(g.grid), dim3(BIG_THREADS), 0, stream, g);
-  else
-    hipLaunchKernelGGL((gemm_bf16_128_kernel<EPI>), dim3(g.grid), dim3(SMALL_THREADS), 0, stream, g);
   return hipGetLastError();
 }
 

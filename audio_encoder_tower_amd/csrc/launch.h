@@ -92,6 +92,10 @@ hipError_t position_table(float* pe, int T, int d, hipStream_t stream);
 // y = GELU(x) elementwise (fp32), for tests of the device erf.
 hipError_t gelu_f32(const float* x, float* y, int64_t n, hipStream_t stream);
 
+// Zero `bytes` (a multiple of 16) at p with a fill kernel (no memset node, so
+// the call is safe inside a captured graph).
+hipError_t fill_zero(void* p, int64_t bytes, hipStream_t stream);
+
 // Plain device copy kernel (16-byte vectors), for calibrating traffic counters.
 hipError_t copy_bytes(void* dst, const void* src, int64_t bytes, hipStream_t stream);
 

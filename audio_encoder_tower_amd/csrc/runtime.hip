@@ -49,11 +49,11 @@ namespace {
 
 enum Kind {
   K_MAPS = 0, K_MEL, K_CONV1, K_CONV2, K_LN, K_QKV, K_ATTN, K_OPROJ, K_FC1, K_FC2, K_FINAL, K_PROJ1, K_PROJ2,
-  K_ZERO, N_KINDS
+  K_ZERO, K_CLEAR, N_KINDS
 };
 const char* kKindNames[N_KINDS] = {"mask_maps", "mel_transpose", "conv1", "conv2", "layernorm", "qkv",
                                    "attention", "o_proj", "fc1", "fc2", "final_ln", "proj1", "proj2",
-                                   "zero_masked"};
+                                   "zero_masked", "scratch_clear"};
 constexpr int PROF_RING = 64;
 
 }  // namespace
@@ -83,17 +83,20 @@ struct aenc_handle {
   float *proj1_b = nullptr, *proj2_b = nullptr;
   float* pe = nullptr;
 
-  // workspace
-  void *melT = nullptr, *g1 = nullptr, *a = nullptr, *qk = nullptr, *vt = nullptr, *hmid = nullptr;
-  float* x = nullptr;
-  int32_t *row_map = nullptr, *inv_map = nullptr, *cu = nullptr, *lens = nullptr, *m_valid = nullptr;
-  int32_t *id_row_map = nullptr, *id_inv_map = nullptr, *id_cu = nullptr, *id_lens = nullptr,
-          *id_m_valid = nullptr;
-  // stacked projector rows (stack > 1): output row -> stacked row, stacked row -> output row, row count
-  int32_t *sk_row_map = nullptr, *sk_inv_map = nullptr, *sk_m_valid = nullptr;
-  int32_t *id_sk_row_map = nullptr, *id_sk_inv_map = nullptr, *id_sk_m_valid = nullptr;
-  // chunked attention: per packed row, the clip-relative keys [key_lo, key_hi) it sees
-  int32_t *key_lo = nullptr, *key_hi = nullptr, *id_key_lo = nullptr, *id_key_hi = nullptr;
+  // workspace: activations and the packing maps (Ws, defined below)
+  struct Ws {
+    void *melT, *g1, *a, *qk, *vt, *hmid;
+    float* x;
+    int64_t ld_vt;
+    // maps written per forward
+    int32_t *row_map, *inv_map, *cu, *lens, *m_valid;
+    int32_t *sk_row_map, *sk_inv_map, *sk_m_valid;   // stacked projector rows (stack > 1)
+    int32_t *key_lo, *key_hi;                        // chunked attention: per packed row, keys [lo, hi)
+    // the same maps for an all-valid batch, built once at create (null: built per forward)
+    const int32_t *id_row_map, *id_inv_map, *id_cu, *id_lens, *id_m_valid;
+    const int32_t *id_sk_row_map, *id_sk_inv_map, *id_sk_m_valid;
+    const int32_t *id_key_lo, *id_key_hi;
+  } w{};
 
   // profiling
   bool prof = false;
@@ -262,6 +265,41 @@ Layout workspace_layout(const aenc_geometry* g) {
   return L;
 }
 
+// Pointers into a workspace laid out by workspace_layout for `batch` clips.
+// The all-valid maps are left null; create() builds them in its own workspace.
+aenc_handle::Ws carve(const aenc_geometry* g, const Layout& L, int batch, char* base) {
+  aenc_handle::Ws w{};
+  w.melT = base + L.off_melT;
+  w.g1 = base + L.off_g1;
+  w.x = (float*)(base + L.off_x);
+  w.a = base + L.off_a;
+  w.qk = base + L.off_qk;
+  w.vt = base + L.off_vt;
+  w.hmid = base + L.off_hmid;
+  w.ld_vt = L.ld_vt;
+  int32_t* maps = (int32_t*)(base + L.off_maps);
+  const int64_t BT = (int64_t)batch * L.T;
+  w.row_map = maps; maps += BT;
+  w.inv_map = maps; maps += L.M_cap;
+  w.cu = maps; maps += batch + 1;
+  w.lens = maps; maps += batch;
+  w.m_valid = maps; maps += 1;
+  // room for the all-valid copies (used by create's workspace only)
+  maps += BT + L.M_cap + batch + 1 + batch + 1;
+  const int k = g->stack > 1 ? g->stack : 1;
+  if (k > 1) {
+    w.sk_row_map = maps; maps += (int64_t)batch * (L.T / k);
+    w.sk_inv_map = maps; maps += L.M_cap / k;
+    w.sk_m_valid = maps; maps += 1;
+    maps += (int64_t)batch * (L.T / k) + L.M_cap / k + 1;
+  }
+  if (g->attn_chunk > 0) {
+    w.key_lo = maps; maps += L.M_cap;
+    w.key_hi = maps; maps += L.M_cap;
+  }
+  return w;
+}
+
 }  // namespace
 
 extern "C" int64_t aenc_workspace_bytes(const aenc_geometry* g) {
@@ -416,46 +454,37 @@ bool build(aenc_handle* h, const aenc_weights* w) {
   HIP_TRY(hipMalloc(&h->ws, h->ws_bytes));
   HIP_TRY(hipMemset(h->ws, 0, h->ws_bytes));
   char* ws = (char*)h->ws;
-  h->melT = ws + Ly.off_melT;
-  h->g1 = ws + Ly.off_g1;
-  h->x = (float*)(ws + Ly.off_x);
-  h->a = ws + Ly.off_a;
-  h->qk = ws + Ly.off_qk;
-  h->vt = ws + Ly.off_vt;
-  h->hmid = ws + Ly.off_hmid;
-  int32_t* maps = (int32_t*)(ws + Ly.off_maps);
+  h->w = carve(&g, Ly, g.batch, ws);
+  aenc_handle::Ws& W = h->w;
+  // the all-valid maps sit right after the per-forward ones (see carve)
+  int32_t* id = (int32_t*)(ws + Ly.off_maps);
   const int64_t BT = (int64_t)g.batch * h->T;
-  h->row_map = maps; maps += BT;
-  h->inv_map = maps; maps += h->M_cap;
-  h->cu = maps; maps += g.batch + 1;
-  h->lens = maps; maps += g.batch;
-  h->m_valid = maps; maps += 1;
-  h->id_row_map = maps; maps += BT;
-  h->id_inv_map = maps; maps += h->M_cap;
-  h->id_cu = maps; maps += g.batch + 1;
-  h->id_lens = maps; maps += g.batch;
-  h->id_m_valid = maps; maps += 1;
-  HIP_TRY(build_row_maps(nullptr, g.batch, h->T, h->id_row_map, h->id_inv_map, h->id_cu, h->id_lens,
-                         h->id_m_valid, nullptr));
+  id += BT + h->M_cap + g.batch + 1 + g.batch + 1;
+  int32_t* id_row_map = id; id += BT;
+  int32_t* id_inv_map = id; id += h->M_cap;
+  int32_t* id_cu = id; id += g.batch + 1;
+  int32_t* id_lens = id; id += g.batch;
+  int32_t* id_m_valid = id; id += 1;
+  HIP_TRY(build_row_maps(nullptr, g.batch, h->T, id_row_map, id_inv_map, id_cu, id_lens, id_m_valid, nullptr));
+  W.id_row_map = id_row_map; W.id_inv_map = id_inv_map; W.id_cu = id_cu; W.id_lens = id_lens;
+  W.id_m_valid = id_m_valid;
   const int k = stack_of(&g);
   if (k > 1) {
-    const int64_t BTk = (int64_t)g.batch * (h->T / k);
-    h->sk_row_map = maps; maps += BTk;
-    h->sk_inv_map = maps; maps += h->M_cap / k;
-    h->sk_m_valid = maps; maps += 1;
-    h->id_sk_row_map = maps; maps += BTk;
-    h->id_sk_inv_map = maps; maps += h->M_cap / k;
-    h->id_sk_m_valid = maps; maps += 1;
-    HIP_TRY(build_stack_maps(h->id_cu, h->id_lens, g.batch, h->T, k, h->id_sk_row_map, h->id_sk_inv_map,
-                             h->id_sk_m_valid, nullptr));
+    int32_t* sk = W.sk_m_valid + 1;
+    int32_t* id_sk_row_map = sk; sk += (int64_t)g.batch * (h->T / k);
+    int32_t* id_sk_inv_map = sk; sk += h->M_cap / k;
+    int32_t* id_sk_m_valid = sk;
+    HIP_TRY(build_stack_maps(id_cu, id_lens, g.batch, h->T, k, id_sk_row_map, id_sk_inv_map, id_sk_m_valid,
+                             nullptr));
+    W.id_sk_row_map = id_sk_row_map; W.id_sk_inv_map = id_sk_inv_map; W.id_sk_m_valid = id_sk_m_valid;
   }
   if (g.attn_chunk > 0) {
-    h->key_lo = maps; maps += h->M_cap;
-    h->key_hi = maps; maps += h->M_cap;
-    h->id_key_lo = maps; maps += h->M_cap;
-    h->id_key_hi = maps; maps += h->M_cap;
-    HIP_TRY(build_chunk_ranges(nullptr, g.batch, h->T, g.attn_chunk, g.attn_chunk_mode, h->id_row_map, h->id_cu,
-                               h->id_key_lo, h->id_key_hi, nullptr));
+    int32_t* r = W.key_hi + h->M_cap;
+    int32_t* id_key_lo = r; r += h->M_cap;
+    int32_t* id_key_hi = r;
+    HIP_TRY(build_chunk_ranges(nullptr, g.batch, h->T, g.attn_chunk, g.attn_chunk_mode, id_row_map, id_cu,
+                               id_key_lo, id_key_hi, nullptr));
+    W.id_key_lo = id_key_lo; W.id_key_hi = id_key_hi;
   }
   HIP_TRY(hipDeviceSynchronize());
   return true;
@@ -497,7 +526,7 @@ extern "C" aenc_handle* aenc_create(const aenc_geometry* g, const aenc_weights* 
   h->device = dev;
   const Layout Ly = workspace_layout(g);
   h->T = Ly.T; h->T8 = Ly.T8; h->C_pad = Ly.C_pad; h->M_cap = Ly.M_cap; h->ld_vt = Ly.ld_vt; h->esz = Ly.esz;
-  h->launches_per_forward = 7 * g->n_layers + 10;
+  h->launches_per_forward = 7 * g->n_layers + 11;
   if (!build(h, w)) {
     std::string msg = g_last_error;
     release(h);
@@ -609,150 +638,155 @@ extern "C" int aenc_handle_geometry(const aenc_handle* h, aenc_geometry* g) {
   return AENC_OK;
 }
 
-extern "C" int aenc_forward(aenc_handle* h, const void* mel, const uint8_t* mask, void* out, void* stream) {
-  if (!h) { set_error("handle is NULL"); return AENC_E_INVAL; }
-  if (!mel || !out) { set_error("mel and out must not be NULL"); return AENC_E_INVAL; }
-  if (((uintptr_t)mel | (uintptr_t)out) & 15) { set_error("mel and out must be 16-byte aligned"); return AENC_E_INVAL; }
+namespace {
+
+// One forward of B clips (B <= the geometry's batch) with workspace w on stream s.
+int forward_impl(aenc_handle* h, const aenc_handle::Ws& w, int B, const void* mel, const uint8_t* mask, void* out,
+                 hipStream_t s, const void* clear, size_t clear_bytes) {
   const aenc_geometry& g = h->g;
-  hipStream_t s = (hipStream_t)stream;
-  const int B = g.batch, T = h->T, F = g.n_frames, d = g.d_model, f = g.d_ffn, C = g.n_mel;
+  const int T = h->T, F = g.n_frames, d = g.d_model, f = g.d_ffn, C = g.n_mel;
+  const int64_t T8 = h->T8;
   const bool bf = g.dtype == AENC_BF16;
   Enq q{h, s, 0, 0};
   if (!q.begin()) { set_error("hipEventRecord failed"); return AENC_E_HIP; }
+  if (clear && !q.done(K_CLEAR, fill_zero((void*)clear, (int64_t)clear_bytes, s), "scratch clear"))
+    return AENC_E_HIP;
 
-  const int32_t *row_map = h->id_row_map, *inv_map = h->id_inv_map, *cu = h->id_cu, *lens = h->id_lens,
-                *mv = h->id_m_valid;
+  // packing maps: the all-valid ones built at create, or built now (a mask,
+  // or a workspace without them)
+  const bool build = mask || !w.id_row_map;
+  const int32_t *row_map = w.id_row_map, *inv_map = w.id_inv_map, *cu = w.id_cu, *lens = w.id_lens,
+                *mv = w.id_m_valid;
   const int k = stack_of(&g);
-  const int32_t *sk_row_map = h->id_sk_row_map, *sk_inv_map = h->id_sk_inv_map, *sk_mv = h->id_sk_m_valid;
-  if (mask) {
-    if (!q.done(K_MAPS, build_row_maps(mask, B, T, h->row_map, h->inv_map, h->cu, h->lens, h->m_valid, s),
-                "mask maps"))
+  const int32_t *sk_row_map = w.id_sk_row_map, *sk_inv_map = w.id_sk_inv_map, *sk_mv = w.id_sk_m_valid;
+  const int32_t *key_lo = w.id_key_lo, *key_hi = w.id_key_hi;
+  if (build) {
+    if (!q.done(K_MAPS, build_row_maps(mask, B, T, w.row_map, w.inv_map, w.cu, w.lens, w.m_valid, s), "mask maps"))
       return AENC_E_HIP;
-    row_map = h->row_map; inv_map = h->inv_map; cu = h->cu; lens = h->lens; mv = h->m_valid;
+    row_map = w.row_map; inv_map = w.inv_map; cu = w.cu; lens = w.lens; mv = w.m_valid;
     if (k > 1) {
-      if (!q.done(K_MAPS, build_stack_maps(cu, lens, B, T, k, h->sk_row_map, h->sk_inv_map, h->sk_m_valid, s),
+      if (!q.done(K_MAPS, build_stack_maps(cu, lens, B, T, k, w.sk_row_map, w.sk_inv_map, w.sk_m_valid, s),
                   "stack maps"))
         return AENC_E_HIP;
-      sk_row_map = h->sk_row_map; sk_inv_map = h->sk_inv_map; sk_mv = h->sk_m_valid;
+      sk_row_map = w.sk_row_map; sk_inv_map = w.sk_inv_map; sk_mv = w.sk_m_valid;
+    }
+    if (g.attn_chunk > 0) {
+      if (!q.done(K_MAPS, build_chunk_ranges(mask, B, T, g.attn_chunk, g.attn_chunk_mode, row_map, cu, w.key_lo,
+                                             w.key_hi, s),
+                  "chunk ranges"))
+        return AENC_E_HIP;
+      key_lo = w.key_lo; key_hi = w.key_hi;
     }
   }
-  const int32_t *key_lo = h->id_key_lo, *key_hi = h->id_key_hi;
-  if (mask && g.attn_chunk > 0) {
-    if (!q.done(K_MAPS, build_chunk_ranges(mask, B, T, g.attn_chunk, g.attn_chunk_mode, row_map, cu, h->key_lo,
-                                           h->key_hi, s),
-                "chunk ranges"))
-      return AENC_E_HIP;
-    key_lo = h->key_lo; key_hi = h->key_hi;
-  }
   // Rows of the packed layout the GEMMs must cover at most (all clips full).
-  const int M_rows = (int)((int64_t)(B - 1) * h->T8 + T);
+  const int M_rows = (int)((int64_t)(B - 1) * T8 + T);
 
-  if (!q.done(K_MEL, mel_transpose(mel, g.dtype, h->melT, B, C, h->C_pad, F, h->g1, g.dtype, d, s), "mel transpose"))
+  if (!q.done(K_MEL, mel_transpose(mel, g.dtype, w.melT, B, C, h->C_pad, F, w.g1, g.dtype, d, s), "mel transpose"))
     return AENC_E_HIP;
 
   // conv1: rows (b, f) read padded frames f, f+1, f+2 (= f-1, f, f+1), K = 3 C_pad
   EpiParams e1{};
   e1.bias = h->conv1_b;
-  e1.c = h->g1;
+  e1.c = w.g1;
   e1.crow = RowMap{F, (int64_t)(F + 2) * d, d, d, nullptr};
   const RowMap a1{F, (int64_t)(F + 2) * h->C_pad, h->C_pad, 0, nullptr};
   hipError_t e;
   if (bf)
-    e = gemm_bf16(EPI_GELU_BF16, (const bf16_t*)h->melT, a1, (const bf16_t*)h->conv1_w, 3 * h->C_pad, B * F, d,
+    e = gemm_bf16(EPI_GELU_BF16, (const bf16_t*)w.melT, a1, (const bf16_t*)h->conv1_w, 3 * h->C_pad, B * F, d,
                   3 * h->C_pad, nullptr, e1, pick_tile(B * F, d), s);
   else
-    e = gemm_f32(EPI_GELU_F32, (const float*)h->melT, a1, (const float*)h->conv1_w, 3 * h->C_pad, B * F, d,
+    e = gemm_f32(EPI_GELU_F32, (const float*)w.melT, a1, (const float*)h->conv1_w, 3 * h->C_pad, B * F, d,
                  3 * h->C_pad, nullptr, e1, s);
   if (!q.done(K_CONV1, e, "conv1")) return AENC_E_HIP;
 
   // conv2: rows (b, t) read conv1 frames 2t-1, 2t, 2t+1 (padded rows 2t .. 2t+2), K = 3 d
   EpiParams e2{};
   e2.bias = h->conv2_b;
-  e2.c = h->x;
+  e2.c = w.x;
   e2.crow = RowMap{INT32_MAX, 0, d, 0, row_map};
   e2.pe = h->pe;
   e2.pe_period = T;
   e2.pe_ld = d;
   const RowMap a2{T, (int64_t)(F + 2) * d, 2 * d, 0, nullptr};
   if (bf)
-    e = gemm_bf16(EPI_GELU_PE_F32, (const bf16_t*)h->g1, a2, (const bf16_t*)h->conv2_w, 3 * d, B * T, d, 3 * d,
+    e = gemm_bf16(EPI_GELU_PE_F32, (const bf16_t*)w.g1, a2, (const bf16_t*)h->conv2_w, 3 * d, B * T, d, 3 * d,
                   nullptr, e2, pick_tile(B * T, d), s);
   else
-    e = gemm_f32(EPI_GELU_PE_F32, (const float*)h->g1, a2, (const float*)h->conv2_w, 3 * d, B * T, d, 3 * d, nullptr,
+    e = gemm_f32(EPI_GELU_PE_F32, (const float*)w.g1, a2, (const float*)h->conv2_w, 3 * d, B * T, d, 3 * d, nullptr,
                  e2, s);
   if (!q.done(K_CONV2, e, "conv2")) return AENC_E_HIP;
 
   const RowMap dense_d = dense_rows(d);
   for (int l = 0; l < g.n_layers; ++l) {
     const aenc_handle::Layer& L = h->layers[l];
-    if (!q.done(K_LN, layernorm(h->x, L.ln1_g, L.ln1_b, h->a, g.dtype, M_rows, mv, d, g.ln_eps, s), "ln1"))
+    if (!q.done(K_LN, layernorm(w.x, L.ln1_g, L.ln1_b, w.a, g.dtype, M_rows, mv, d, g.ln_eps, s), "ln1"))
       return AENC_E_HIP;
     EpiParams eq{};
     eq.bias = L.qkv_b;
-    eq.c = h->qk;
+    eq.c = w.qk;
     if (bf) {
       eq.crow = dense_rows(2 * d);
       eq.n_split = 2 * d;
-      eq.vt = (bf16_t*)h->vt;
-      eq.ld_vt = h->ld_vt;
+      eq.vt = (bf16_t*)w.vt;
+      eq.ld_vt = w.ld_vt;
       eq.q_cols = d;                 // the attention kernel takes Q in base-2 score units
       eq.q_scale = ATT_Q_SCALE;
-      e = gemm_bf16(EPI_QKV_BF16, (const bf16_t*)h->a, dense_d, (const bf16_t*)L.qkv_w, d, M_rows, 3 * d, d, mv, eq,
+      e = gemm_bf16(EPI_QKV_BF16, (const bf16_t*)w.a, dense_d, (const bf16_t*)L.qkv_w, d, M_rows, 3 * d, d, mv, eq,
                     pick_tile(M_rows, 3 * d), s);
     } else {
       eq.crow = dense_rows(3 * d);
-      e = gemm_f32(EPI_STORE_F32, (const float*)h->a, dense_d, (const float*)L.qkv_w, d, M_rows, 3 * d, d, mv, eq, s);
+      e = gemm_f32(EPI_STORE_F32, (const float*)w.a, dense_d, (const float*)L.qkv_w, d, M_rows, 3 * d, d, mv, eq, s);
     }
     if (!q.done(K_QKV, e, "qkv")) return AENC_E_HIP;
 
     if (bf)
-      e = attention_bf16((const bf16_t*)h->qk, 2 * d, (const bf16_t*)h->vt, h->ld_vt, cu, lens, B, T, g.n_heads,
-                         (bf16_t*)h->a, d, key_lo, key_hi, s);
+      e = attention_bf16((const bf16_t*)w.qk, 2 * d, (const bf16_t*)w.vt, w.ld_vt, cu, lens, B, T, g.n_heads,
+                         (bf16_t*)w.a, d, key_lo, key_hi, s);
     else
-      e = attention_f32((const float*)h->qk, 3 * d, cu, lens, B, T, g.n_heads, (float*)h->a, d, key_lo, key_hi, s);
+      e = attention_f32((const float*)w.qk, 3 * d, cu, lens, B, T, g.n_heads, (float*)w.a, d, key_lo, key_hi, s);
     if (!q.done(K_ATTN, e, "attention")) return AENC_E_HIP;
 
     EpiParams eo{};
     eo.bias = L.o_b;
-    eo.c = h->x;
+    eo.c = w.x;
     eo.crow = dense_d;
-    e = bf ? gemm_bf16(EPI_RESID_F32, (const bf16_t*)h->a, dense_d, (const bf16_t*)L.o_w, d, M_rows, d, d, mv, eo,
+    e = bf ? gemm_bf16(EPI_RESID_F32, (const bf16_t*)w.a, dense_d, (const bf16_t*)L.o_w, d, M_rows, d, d, mv, eo,
                        pick_tile(M_rows, d), s)
-           : gemm_f32(EPI_RESID_F32, (const float*)h->a, dense_d, (const float*)L.o_w, d, M_rows, d, d, mv, eo, s);
+           : gemm_f32(EPI_RESID_F32, (const float*)w.a, dense_d, (const float*)L.o_w, d, M_rows, d, d, mv, eo, s);
     if (!q.done(K_OPROJ, e, "o_proj")) return AENC_E_HIP;
 
-    if (!q.done(K_LN, layernorm(h->x, L.ln2_g, L.ln2_b, h->a, g.dtype, M_rows, mv, d, g.ln_eps, s), "ln2"))
+    if (!q.done(K_LN, layernorm(w.x, L.ln2_g, L.ln2_b, w.a, g.dtype, M_rows, mv, d, g.ln_eps, s), "ln2"))
       return AENC_E_HIP;
 
     EpiParams ef1{};
     ef1.bias = L.fc1_b;
-    ef1.c = h->hmid;
+    ef1.c = w.hmid;
     ef1.crow = dense_rows(f);
-    e = bf ? gemm_bf16(EPI_GELU_BF16, (const bf16_t*)h->a, dense_d, (const bf16_t*)L.fc1_w, d, M_rows, f, d, mv, ef1,
+    e = bf ? gemm_bf16(EPI_GELU_BF16, (const bf16_t*)w.a, dense_d, (const bf16_t*)L.fc1_w, d, M_rows, f, d, mv, ef1,
                        pick_tile(M_rows, f), s)
-           : gemm_f32(EPI_GELU_F32, (const float*)h->a, dense_d, (const float*)L.fc1_w, d, M_rows, f, d, mv, ef1, s);
+           : gemm_f32(EPI_GELU_F32, (const float*)w.a, dense_d, (const float*)L.fc1_w, d, M_rows, f, d, mv, ef1, s);
     if (!q.done(K_FC1, e, "fc1")) return AENC_E_HIP;
 
     EpiParams ef2{};
     ef2.bias = L.fc2_b;
-    ef2.c = h->x;
+    ef2.c = w.x;
     ef2.crow = dense_d;
-    e = bf ? gemm_bf16(EPI_RESID_F32, (const bf16_t*)h->hmid, dense_rows(f), (const bf16_t*)L.fc2_w, f, M_rows, d, f,
+    e = bf ? gemm_bf16(EPI_RESID_F32, (const bf16_t*)w.hmid, dense_rows(f), (const bf16_t*)L.fc2_w, f, M_rows, d, f,
                        mv, ef2, pick_tile(M_rows, d), s)
-           : gemm_f32(EPI_RESID_F32, (const float*)h->hmid, dense_rows(f), (const float*)L.fc2_w, f, M_rows, d, f, mv,
+           : gemm_f32(EPI_RESID_F32, (const float*)w.hmid, dense_rows(f), (const float*)L.fc2_w, f, M_rows, d, f, mv,
                       ef2, s);
     if (!q.done(K_FC2, e, "fc2")) return AENC_E_HIP;
   }
 
   if (!g.proj_hidden) {
-    if (!q.done(K_FINAL, final_ln_out(h->x, row_map, h->lnf_g, h->lnf_b, out, g.out_dtype, B, T, g.pool_step, d,
+    if (!q.done(K_FINAL, final_ln_out(w.x, row_map, h->lnf_g, h->lnf_b, out, g.out_dtype, B, T, g.pool_step, d,
                                       g.ln_eps, s), "final ln"))
       return AENC_E_HIP;
     return AENC_OK;
   }
 
   const int ph = g.proj_hidden, po = g.proj_out;
-  if (!q.done(K_FINAL, layernorm(h->x, h->lnf_g, h->lnf_b, h->a, g.dtype, M_rows, mv, d, g.ln_eps, s), "final ln"))
+  if (!q.done(K_FINAL, layernorm(w.x, h->lnf_g, h->lnf_b, w.a, g.dtype, M_rows, mv, d, g.ln_eps, s), "final ln"))
     return AENC_E_HIP;
   // Projector rows: the packed LN rows themselves, or (stack k) runs of k
   // packed rows read as one k*d-wide row. Clip starts are multiples of 8, so
@@ -763,11 +797,11 @@ extern "C" int aenc_forward(aenc_handle* h, const void* mel, const uint8_t* mask
   const int32_t* mvp = k > 1 ? sk_mv : mv;
   EpiParams ep1{};
   ep1.bias = h->proj1_b;
-  ep1.c = h->hmid;
+  ep1.c = w.hmid;
   ep1.crow = dense_rows(ph);
-  e = bf ? gemm_bf16(EPI_GELU_BF16, (const bf16_t*)h->a, dense_rows(pin), (const bf16_t*)h->proj1_w, pin, Mp, ph,
+  e = bf ? gemm_bf16(EPI_GELU_BF16, (const bf16_t*)w.a, dense_rows(pin), (const bf16_t*)h->proj1_w, pin, Mp, ph,
                      pin, mvp, ep1, pick_tile(Mp, ph), s)
-         : gemm_f32(EPI_GELU_F32, (const float*)h->a, dense_rows(pin), (const float*)h->proj1_w, pin, Mp, ph, pin, mvp,
+         : gemm_f32(EPI_GELU_F32, (const float*)w.a, dense_rows(pin), (const float*)h->proj1_w, pin, Mp, ph, pin, mvp,
                     ep1, s);
   if (!q.done(K_PROJ1, e, "proj1")) return AENC_E_HIP;
 
@@ -777,9 +811,9 @@ extern "C" int aenc_forward(aenc_handle* h, const void* mel, const uint8_t* mask
   // packed (or stacked) row -> output row b * T_out + j, or -1 (not written)
   ep2.crow = RowMap{INT32_MAX, 0, po, 0, k > 1 ? sk_inv_map : inv_map};
   const int epi2 = g.out_dtype == AENC_BF16 ? EPI_STORE_BF16 : EPI_STORE_F32;
-  e = bf ? gemm_bf16(epi2, (const bf16_t*)h->hmid, dense_rows(ph), (const bf16_t*)h->proj2_w, ph, Mp, po, ph, mvp,
+  e = bf ? gemm_bf16(epi2, (const bf16_t*)w.hmid, dense_rows(ph), (const bf16_t*)h->proj2_w, ph, Mp, po, ph, mvp,
                      ep2, pick_tile(Mp, po), s)
-         : gemm_f32(epi2, (const float*)h->hmid, dense_rows(ph), (const float*)h->proj2_w, ph, Mp, po, ph, mvp, ep2, s);
+         : gemm_f32(epi2, (const float*)w.hmid, dense_rows(ph), (const float*)h->proj2_w, ph, Mp, po, ph, mvp, ep2, s);
   if (!q.done(K_PROJ2, e, "proj2")) return AENC_E_HIP;
   if (mask) {
     const int32_t* zmap = k > 1 ? sk_row_map : row_map;
@@ -787,4 +821,13 @@ extern "C" int aenc_forward(aenc_handle* h, const void* mel, const uint8_t* mask
       return AENC_E_HIP;
   }
   return AENC_OK;
+}
+
+}  // namespace
+
+extern "C" int aenc_forward(aenc_handle* h, const void* mel, const uint8_t* mask, void* out, void* stream) {
+  if (!h) { set_error("handle is NULL"); return AENC_E_INVAL; }
+  if (!mel || !out) { set_error("mel and out must not be NULL"); return AENC_E_INVAL; }
+  if (((uintptr_t)mel | (uintptr_t)out) & 15) { set_error("mel and out must be 16-byte aligned"); return AENC_E_INVAL; }
+  return forward_impl(h, h->w, h->g.batch, mel, mask, out, (hipStream_t)stream, nullptr, 0);
 }

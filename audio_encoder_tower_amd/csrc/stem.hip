@@ -1,6 +1,8 @@
 // Data-movement kernels around the encoder: the mel transpose that feeds the
 // implicit-GEMM convolutions, the packing maps of a key mask, weight repacks
 // and the sinusoidal position table.
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 
@@ -281,6 +283,19 @@ __global__ void gelu_kernel(const float* x, float* y, int64_t n) {
 hipError_t gelu_f32(const float* x, float* y, int64_t n, hipStream_t stream) {
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(gelu_kernel, dim3(1024), dim3(256), 0, stream, x, y, n);
+  return hipGetLastError();
+}
+
+__global__ void fill_zero_kernel(u32x4* __restrict__ p, int64_t n16) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n16; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
+hipError_t fill_zero(void* p, int64_t bytes, hipStream_t stream) {
+  if (bytes <= 0 || bytes % 16 != 0 || ((uintptr_t)p & 15)) return hipErrorInvalidValue;
+  const int64_t n16 = bytes / 16;
+  const int64_t blocks = std::min<int64_t>((n16 + 255) / 256, 4096);
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (u32x4*)p, n16);
   return hipGetLastError();
 }
 

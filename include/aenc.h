@@ -193,6 +193,7 @@ const char *aenc_profile_kind_name(int kind);
 /* The geometry a handle was created with (NULL arguments: AENC_E_INVAL). */
 int aenc_handle_geometry(const aenc_handle *h, aenc_geometry *g);
 
+
 /* ---------------------------------------------------------------------------
  * Embeddings cache: encoder outputs kept on the device under caller-given
  * 64-bit content keys (for instance a hash of the clip's audio and length),

@@ -56,6 +56,8 @@ GEMM_SHAPES = [
     (777, 1284, 4160),    # ragged M and N, 65 slices: a partial trip of the 6-slice buffer cycle
     (70, 196, 64),        # N = 4 mod 8: 4-column tails and rows not 16-byte aligned
     (4000, 4920, 1280),   # 256x256: 40 tiles per XCD, the last 8 run as 128-column halves (ragged M, N)
+    (22700, 760, 128),    # 256x256: 267 tiles (not a multiple of 8): 34 or 33 per XCD, tails of 2 and 1 split
+    (24000, 3840, 64),    # 256x256: 1410 tiles: 177 per XCD (tail 17, whole) or 176 (tail 16, split)
 ]
 
 
