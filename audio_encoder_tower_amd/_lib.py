@@ -14,6 +14,8 @@ LIB_PATH = os.path.join(PKG, "libaenc.so")
 
 AENC_F32 = 0
 AENC_BF16 = 1
+# bytes of the static scratch array of aenc_forward_noalloc (AENC_NOALLOC_SCRATCH_BYTES)
+AENC_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 STATUS = {0: "AENC_OK", -1: "AENC_E_INVAL", -2: "AENC_E_UNSUPPORTED", -3: "AENC_E_NOMEM",
           -4: "AENC_E_DEVICE", -5: "AENC_E_HIP"}
@@ -81,6 +83,8 @@ SIGNATURES = {
     "aenc_k_copy_stream": (c_int, [c_void_p, c_void_p, c_int64, c_void_p]),
     "aenc_k_mfma_loop": (c_int, [c_void_p, c_int, c_int, c_void_p]),
     "aenc_handle_geometry": (c_int, [c_void_p, POINTER(Geometry)]),
+    "aenc_forward_noalloc": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "aenc_noalloc_scratch_bytes": (c_int64, [POINTER(Geometry), c_int]),
     # embeddings cache (aenc.h)
     "aenc_cache_create": (c_void_p, [c_int64, c_int64]),
     "aenc_cache_destroy": (None, [c_void_p]),

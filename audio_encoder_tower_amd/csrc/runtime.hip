@@ -15,6 +15,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -58,6 +59,36 @@ constexpr int PROF_RING = 64;
 
 }  // namespace
 
+// One array per GPU the library runs on, held until the process ends. Calls on
+// one GPU share it (and race if they overlap); it keeps the last call's
+// contents, so each call clears the part it uses first.
+static __device__ __align__(256) unsigned char scratch[AENC_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_ptr;   // per device: the address of `scratch` there (null until looked up)
+
+// The device address of this GPU's copy of `scratch`, looked up once per device
+// (with that device current) and kept; the array's name in host code is not it.
+bool scratch_of_device(int dev, void** ptr) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if ((int)g_scratch_ptr.size() <= dev) g_scratch_ptr.resize(dev + 1, nullptr);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      set_error("hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+      return false;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return true;
+}
+
+}  // namespace
+
 struct aenc_handle {
   aenc_geometry g{};
   int device = 0;
@@ -97,6 +128,9 @@ struct aenc_handle {
     const int32_t *id_sk_row_map, *id_sk_inv_map, *id_sk_m_valid;
     const int32_t *id_key_lo, *id_key_hi;
   } w{};
+
+  // this device's copy of the static scratch array of aenc_forward_noalloc
+  void* scratch = nullptr;
 
   // profiling
   bool prof = false;
@@ -521,9 +555,13 @@ extern "C" aenc_handle* aenc_create(const aenc_geometry* g, const aenc_weights* 
     return nullptr;
   }
 
+  void* scratch_ptr = nullptr;
+  if (!scratch_of_device(dev, &scratch_ptr)) return nullptr;
+
   aenc_handle* h = new aenc_handle();
   h->g = *g;
   h->device = dev;
+  h->scratch = scratch_ptr;
   const Layout Ly = workspace_layout(g);
   h->T = Ly.T; h->T8 = Ly.T8; h->C_pad = Ly.C_pad; h->M_cap = Ly.M_cap; h->ld_vt = Ly.ld_vt; h->esz = Ly.esz;
   h->launches_per_forward = 7 * g->n_layers + 11;
@@ -830,4 +868,39 @@ extern "C" int aenc_forward(aenc_handle* h, const void* mel, const uint8_t* mask
   if (!mel || !out) { set_error("mel and out must not be NULL"); return AENC_E_INVAL; }
   if (((uintptr_t)mel | (uintptr_t)out) & 15) { set_error("mel and out must be 16-byte aligned"); return AENC_E_INVAL; }
   return forward_impl(h, h->w, h->g.batch, mel, mask, out, (hipStream_t)stream, nullptr, 0);
+}
+
+// ---------------------------------------------------------------------------
+// forward without allocation: the workspace is a static device array
+// ---------------------------------------------------------------------------
+
+extern "C" int64_t aenc_noalloc_scratch_bytes(const aenc_geometry* g, int n_clips) {
+  if (aenc_validate(g) != AENC_OK) return -1;
+  if (n_clips < 1 || n_clips > g->batch) { set_error("n_clips %d outside 1..batch (%d)", n_clips, g->batch); return -1; }
+  aenc_geometry gb = *g;
+  gb.batch = n_clips;
+  return (int64_t)workspace_layout(&gb).total;
+}
+
+extern "C" int aenc_forward_noalloc(aenc_handle* h, int n_clips, const void* mel, const uint8_t* mask, void* out,
+                                    void* stream) {
+  if (!h) { set_error("handle is NULL"); return AENC_E_INVAL; }
+  if (!mel || !out) { set_error("mel and out must not be NULL"); return AENC_E_INVAL; }
+  if (((uintptr_t)mel | (uintptr_t)out) & 15) { set_error("mel and out must be 16-byte aligned"); return AENC_E_INVAL; }
+  if (n_clips < 1 || n_clips > h->g.batch) {
+    set_error("n_clips %d outside 1..%d (the handle's batch)", n_clips, h->g.batch);
+    return AENC_E_INVAL;
+  }
+  if (!h->scratch) { set_error("no scratch array on this handle's device"); return AENC_E_DEVICE; }
+  aenc_geometry gb = h->g;
+  gb.batch = n_clips;
+  const Layout Ly = workspace_layout(&gb);
+  if (Ly.total > (size_t)AENC_NOALLOC_SCRATCH_BYTES) {
+    set_error("%d clip(s) of this geometry need %zu bytes of workspace, over the %lld-byte static scratch of "
+              "aenc_forward_noalloc; pass fewer clips",
+              n_clips, Ly.total, (long long)AENC_NOALLOC_SCRATCH_BYTES);
+    return AENC_E_INVAL;
+  }
+  const aenc_handle::Ws w = carve(&gb, Ly, n_clips, (char*)h->scratch);
+  return forward_impl(h, w, n_clips, mel, mask, out, (hipStream_t)stream, h->scratch, Ly.total);
 }

@@ -193,6 +193,35 @@ const char *aenc_profile_kind_name(int kind);
 /* The geometry a handle was created with (NULL arguments: AENC_E_INVAL). */
 int aenc_handle_geometry(const aenc_handle *h, aenc_geometry *g);
 
+/* ---------------------------------------------------------------------------
+ * Forward without allocation, for callers that cannot allocate device memory
+ * while they run (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the activations live in a static device array of
+ * AENC_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends, instead of the handle's workspace.
+ *
+ * aenc_forward_noalloc runs aenc_forward's kernels on the first n_clips clips
+ * of the buffers (1 <= n_clips <= the handle's batch): mel [n_clips, n_mel,
+ * n_frames], mask [n_clips, T] or NULL, out [n_clips, T_out, D_out], in the
+ * layouts and types of aenc_forward, and enqueues on `stream` without
+ * synchronising. It allocates nothing and calls no allocating routine; the
+ * packing maps are built into the array on every call, and the part of the
+ * array a call uses is cleared first by a fill kernel (the array keeps the
+ * last call's contents otherwise). Every call on one GPU shares that GPU's
+ * array, whatever the handle: calls that overlap in time on one GPU race and
+ * must be ordered by the caller (one stream, or events). Returns AENC_OK,
+ * AENC_E_INVAL (NULL handle or pointer, misaligned pointer, n_clips out of
+ * range, or a workspace for n_clips clips over AENC_NOALLOC_SCRATCH_BYTES:
+ * aenc_last_error() gives the size needed) or AENC_E_HIP (launch failure).
+ * A Whisper-large clip (3000 frames, d_model 1280, FFN 5120) needs about
+ * 47 MB, so the array holds one such clip per call.
+ *
+ * aenc_noalloc_scratch_bytes: the bytes n_clips clips of g need in the array
+ * (host only; -1 for an invalid geometry or n_clips outside 1..g->batch). */
+#define AENC_NOALLOC_SCRATCH_BYTES (64LL << 20)
+int aenc_forward_noalloc(aenc_handle *h, int n_clips, const void *mel, const uint8_t *mask, void *out,
+                         void *stream);
+int64_t aenc_noalloc_scratch_bytes(const aenc_geometry *g, int n_clips);
 
 /* ---------------------------------------------------------------------------
  * Embeddings cache: encoder outputs kept on the device under caller-given
