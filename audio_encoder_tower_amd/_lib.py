@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(PKG, "libaenc.so")
 AENC_F32 = 0
 AENC_BF16 = 1
 # bytes of the static scratch array of aenc_forward_noalloc (AENC_NOALLOC_SCRATCH_BYTES)
-AENC_NOALLOC_SCRATCH_BYTES = 64 << 20
+AENC_NOALLOC_SCRATCH_BYTES = 96 << 20
 
 STATUS = {0: "AENC_OK", -1: "AENC_E_INVAL", -2: "AENC_E_UNSUPPORTED", -3: "AENC_E_NOMEM",
           -4: "AENC_E_DEVICE", -5: "AENC_E_HIP"}

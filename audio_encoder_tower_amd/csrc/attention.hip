@@ -9,7 +9,8 @@
 // for chunked attention, each query's key range.
 //
 // bf16 kernel (flash-style, one pass over the keys with an online softmax):
-//   - workgroup = (128-query tile, head, clip), four wave64s with 32 queries each;
+//   - workgroup = (128-query tile, head, clip), four wave64s with 32 queries each
+//     (two wave64s and 64 queries when the 4-wave grid would leave CUs idle);
 //   - 64-key tiles of K (row-major) and V (already transposed by the QKV
 //     GEMM's epilogue) are staged in LDS, double-buffered through registers;
 //   - S^T = K Q^T on v_mfma_f32_32x32x16_bf16, so each lane holds 32 scores of
@@ -34,7 +35,7 @@
 
 namespace aenc {
 
-constexpr int ATT_BQ = 128;
+constexpr int ATT_BQ = 128;   // queries per workgroup of 4 waves (32 per wave)
 constexpr int ATT_BK = 64;
 constexpr int ATT_D = 64;
 
@@ -47,8 +48,10 @@ __device__ __forceinline__ int att_swz(int row, int chunk) { return chunk ^ ((ro
 // [key_lo[r], key_hi[r]), non-empty and non-decreasing in i (the chunk rules);
 // the workgroup walks the key tiles between its first query's key_lo and its
 // last query's key_hi and masks per query.
-template <bool RANGED>
-__global__ __launch_bounds__(256) void attention_bf16_kernel(const bf16_t* __restrict__ qk, int64_t ld_qk,
+// NW waves per workgroup (4, or 2 for short batches, whose 4-wave grids leave
+// CUs idle): BQ = 32 NW queries per workgroup.
+template <bool RANGED, int NW>
+__global__ __launch_bounds__(64 * NW) void attention_bf16_kernel(const bf16_t* __restrict__ qk, int64_t ld_qk,
                                                              const bf16_t* __restrict__ vt, int64_t ld_vt,
                                                              const int32_t* __restrict__ starts,
                                                              const int32_t* __restrict__ lens, int d,
@@ -82,7 +85,8 @@ __global__ __launch_bounds__(256) void attention_bf16_kernel(const bf16_t* __res
   }
   const int start = starts[b];
   const int len = lens[b];
-  const int q0 = qb * ATT_BQ;
+  constexpr int BQ = 32 * NW, THREADS = 64 * NW, CH = 512 / THREADS;   // CH: 16-byte chunks per thread and tile
+  const int q0 = qb * BQ;
   if (q0 >= len) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -94,7 +98,7 @@ __global__ __launch_bounds__(256) void attention_bf16_kernel(const bf16_t* __res
     k_lo = key_lo[start + min(qi, len - 1)];
     k_hi = key_hi[start + min(qi, len - 1)];
     kt_first = key_lo[start + q0] / ATT_BK;
-    kt_last = (key_hi[start + min(q0 + ATT_BQ, len) - 1] - 1) / ATT_BK;
+    kt_last = (key_hi[start + min(q0 + BQ, len) - 1] - 1) / ATT_BK;
   }
 
   // Q fragments (B operand of S^T = K Q^T): dims 16s + 8hh .. +7. Q arrives
@@ -106,7 +110,7 @@ __global__ __launch_bounds__(256) void attention_bf16_kernel(const bf16_t* __res
     for (int s = 0; s < 4; ++s) qf[s] = *(const bf16x8*)(qrow + 16 * s);
   }
 
-  // Cooperative tile loads: two 16-byte chunks of K and two of V^T per thread.
+  // Cooperative tile loads: CH 16-byte chunks of K and CH of V^T per thread.
   // Whole tiles come through buffer loads based at the clip's first row: the
   // per-lane offset is fixed and the tile's key offset rides in the scalar
   // offset, so a tile costs no address arithmetic. A tile that runs past the
@@ -119,19 +123,19 @@ __global__ __launch_bounds__(256) void attention_bf16_kernel(const bf16_t* __res
                                                                        0x7fffffff, 0x00020000);
   const __amdgpu_buffer_rsrc_t rsv = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(vbase), (short)0,
                                                                        0x7fffffff, 0x00020000);
-  uint32_t koff[2], voff[2];
+  uint32_t koff[CH], voff[CH];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int c = tid + 256 * i;
+  for (int i = 0; i < CH; ++i) {
+    const int c = tid + THREADS * i;
     koff[i] = (uint32_t)(((c >> 3) * ld_qk + (c & 7) * 8) * 2);
     voff[i] = (uint32_t)(((c >> 3) * ld_vt + (c & 7) * 8) * 2);
   }
-  u32x4 rk[2], rv[2];
+  u32x4 rk[CH], rv[CH];
   auto gload = [&](int k0, auto ragged) {
     constexpr bool RAGGED = decltype(ragged)::value;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + 256 * i;
+    for (int i = 0; i < CH; ++i) {
+      const int c = tid + THREADS * i;
       const int key = c >> 3, ch = c & 7;
       if (RAGGED) {
         rk[i] = *(const u32x4*)(kbase + (int64_t)min(k0 + key, len - 1) * ld_qk + ch * 8);
@@ -153,8 +157,8 @@ __global__ __launch_bounds__(256) void attention_bf16_kernel(const bf16_t* __res
   };
   auto lstore = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + 256 * i;
+    for (int i = 0; i < CH; ++i) {
+      const int c = tid + THREADS * i;
       const int key = c >> 3, ch = c & 7;
       *(u32x4*)(&Ks[buf][key * ATT_D + att_swz(key, ch) * 8]) = rk[i];
       // Keys 8kc .. 8kc+7 are two groups of four; within each 16-key block the
@@ -325,16 +329,28 @@ hipError_t attention_bf16(const bf16_t* qk, int64_t ld_qk, const bf16_t* vt, int
   // buffer-load offsets within one clip stay below 2^31 bytes
   if ((int64_t)(max_len + ATT_BK) * ld_qk * 2 >= INT32_MAX || (int64_t)ATT_D * ld_vt * 2 >= INT32_MAX)
     return hipErrorInvalidValue;
-  const int n_qb = (max_len + ATT_BQ - 1) / ATT_BQ;
+  // 4-wave workgroups of 128 queries, or 2-wave ones of 64 when the 4-wave
+  // grid would give the 256 CUs fewer than two workgroups each
+  const int n_qb4 = (max_len + ATT_BQ - 1) / ATT_BQ;
+  const bool two = (int64_t)n_qb4 * n_heads * n_clips < 512;
+  const int n_qb = two ? (max_len + ATT_BQ / 2 - 1) / (ATT_BQ / 2) : n_qb4;
   if (key_lo) {
-    hipLaunchKernelGGL(attention_bf16_kernel<true>, dim3(n_heads, n_clips, n_qb), dim3(256), 0, stream, qk, ld_qk,
-                       vt, ld_vt, start, len, n_heads * ATT_D, o, ld_o, key_lo, key_hi, n_qb, n_clips);
+    if (two)
+      hipLaunchKernelGGL((attention_bf16_kernel<true, 2>), dim3(n_heads, n_clips, n_qb), dim3(128), 0, stream, qk,
+                         ld_qk, vt, ld_vt, start, len, n_heads * ATT_D, o, ld_o, key_lo, key_hi, n_qb, n_clips);
+    else
+      hipLaunchKernelGGL((attention_bf16_kernel<true, 4>), dim3(n_heads, n_clips, n_qb), dim3(256), 0, stream, qk,
+                         ld_qk, vt, ld_vt, start, len, n_heads * ATT_D, o, ld_o, key_lo, key_hi, n_qb, n_clips);
   } else {
     const int64_t n = (int64_t)n_qb * n_heads * n_clips;
     if (n > INT32_MAX - 8) return hipErrorInvalidValue;
     const int grid = (int)((n + 7) / 8 * 8);
-    hipLaunchKernelGGL(attention_bf16_kernel<false>, dim3(grid), dim3(256), 0, stream, qk, ld_qk, vt, ld_vt, start,
-                       len, n_heads * ATT_D, o, ld_o, nullptr, nullptr, n_qb, n_clips);
+    if (two)
+      hipLaunchKernelGGL((attention_bf16_kernel<false, 2>), dim3(grid), dim3(128), 0, stream, qk, ld_qk, vt, ld_vt,
+                         start, len, n_heads * ATT_D, o, ld_o, nullptr, nullptr, n_qb, n_clips);
+    else
+      hipLaunchKernelGGL((attention_bf16_kernel<false, 4>), dim3(grid), dim3(256), 0, stream, qk, ld_qk, vt, ld_vt,
+                         start, len, n_heads * ATT_D, o, ld_o, nullptr, nullptr, n_qb, n_clips);
   }
   return hipGetLastError();
 }

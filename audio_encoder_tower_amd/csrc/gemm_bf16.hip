@@ -58,6 +58,11 @@ struct GemmArgs {
   uint32_t a_bytes, w_bytes;   // extents of A and W reachable through the row maps
   int tiles_n;
   EpiParams epi;
+  // 128x128 kernel only: split-K. `splits` launches' worth of tiles, split s
+  // reducing K columns [s K, (s + 1) K) (K above is per split) and writing
+  // its partial product (EPI_STORE_F32, no bias) at C offset s * c_split_stride.
+  int splits;
+  int64_t c_split_stride;
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -131,9 +136,11 @@ __device__ __forceinline__ void tile_group_order(int tiles_m, int tiles_n, int t
 // 16 tiles on its 32 CUs, those tiles run as two 128-column halves each
 // (`half` 0 or 1; -1 for a whole tile). False for workgroups past the work.
 template <bool SPLIT>
-__device__ __forceinline__ bool tile_of_block(const GemmArgs& g, int M, int BM, int& tm, int& tn, int& half) {
+__device__ __forceinline__ bool tile_of_block(const GemmArgs& g, int M, int BM, int& tm, int& tn, int& half,
+                                              int* ksplit = nullptr) {
   const int tiles_m = (M + BM - 1) / BM;
-  const int total = tiles_m * g.tiles_n;
+  const int per_split = tiles_m * g.tiles_n;
+  const int total = per_split * (ksplit ? g.splits : 1);
   const int x = blockIdx.x % N_XCD, i = blockIdx.x / N_XCD;
   const int base = total / N_XCD, rem = total % N_XCD;
   const int cnt = base + (x < rem ? 1 : 0), first = x * base + min(x, rem);
@@ -150,7 +157,12 @@ __device__ __forceinline__ bool tile_of_block(const GemmArgs& g, int M, int BM, 
     half = (i - full) & 1;
   }
   if (t >= cnt) return false;
-  tile_group_order(tiles_m, g.tiles_n, first + t, tm, tn);
+  int tile = first + t;
+  if (ksplit) {
+    *ksplit = tile / per_split;   // the split is the slowest index: an XCD's range stays within few splits
+    tile -= *ksplit * per_split;
+  }
+  tile_group_order(tiles_m, g.tiles_n, tile, tm, tn);
   return true;
 }
 
@@ -356,7 +368,8 @@ __device__ __forceinline__ void small_slice(f32x16 (&acc)[SM][SN], const bf16_t*
   __builtin_amdgcn_s_setprio(0);
 }
 
-template <int EPI>
+// SPLITK: the launch splits K (GemmArgs.splits); a separate instantiation.
+template <int EPI, bool SPLITK>
 __global__ __launch_bounds__(SMALL_THREADS) void gemm_bf16_128_kernel(GemmArgs g) {
   constexpr int BM = 128, BN = 128, WM = 64, WN = 64;
   constexpr int SM = WM / 32, SN = WN / 32;
@@ -364,9 +377,11 @@ __global__ __launch_bounds__(SMALL_THREADS) void gemm_bf16_128_kernel(GemmArgs g
   __shared__ __attribute__((aligned(16))) bf16_t buf1[(BM + BN) * GEMM_BK];
 
   const int M = g.m_dev ? min(*g.m_dev, g.M) : g.M;
-  int tm, tn, half;
-  if (!tile_of_block<false>(g, M, BM, tm, tn, half)) return;
+  int tm, tn, half, ks = 0;
+  if (!tile_of_block<false>(g, M, BM, tm, tn, half, SPLITK ? &ks : nullptr)) return;
   const int m0 = tm * BM, n0 = tn * BN;
+  // split ks reads K columns from ks * K on: a scalar byte offset on every copy
+  const uint32_t kb0 = SPLITK ? (uint32_t)ks * (uint32_t)g.K * 2u : 0u;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -392,7 +407,7 @@ __global__ __launch_bounds__(SMALL_THREADS) void gemm_bf16_128_kernel(GemmArgs g
 
   const int nk = g.K / GEMM_BK;
   {
-    const SmallCopy first{ra, rw, &pa, &pw, 0, a0, b0, wave, true};
+    const SmallCopy first{ra, rw, &pa, &pw, kb0, a0, b0, wave, true};
     first(0);
     first(1);
     first(2);
@@ -405,12 +420,12 @@ __global__ __launch_bounds__(SMALL_THREADS) void gemm_bf16_128_kernel(GemmArgs g
   for (; kt + 1 < nk; kt += 2) {
     // slice kt from buffer 0 while slice kt+1 lands in buffer 1
     small_slice<SM, SN>(acc, a0, b0, a_row0, b_row0, fr, fk,
-                        SmallCopy{ra, rw, &pa, &pw, (uint32_t)(kt + 1) * GEMM_BK * 2, a1, b1, wave, true});
+                        SmallCopy{ra, rw, &pa, &pw, kb0 + (uint32_t)(kt + 1) * GEMM_BK * 2, a1, b1, wave, true});
     wait_copies();
     __syncthreads();
     // slice kt+1 from buffer 1 while slice kt+2 (if any) lands in buffer 0
     small_slice<SM, SN>(acc, a1, b1, a_row0, b_row0, fr, fk,
-                        SmallCopy{ra, rw, &pa, &pw, (uint32_t)(kt + 2) * GEMM_BK * 2, a0, b0, wave, kt + 2 < nk});
+                        SmallCopy{ra, rw, &pa, &pw, kb0 + (uint32_t)(kt + 2) * GEMM_BK * 2, a0, b0, wave, kt + 2 < nk});
     wait_copies();
     __syncthreads();
   }
@@ -421,7 +436,13 @@ __global__ __launch_bounds__(SMALL_THREADS) void gemm_bf16_128_kernel(GemmArgs g
 
   constexpr int SW = WN;
   float* slab = (float*)(wave < 2 ? buf0 : buf1) + (wave & 1) * (32 * (SW + 4));
-  store_tile<EPI, SM, SN, SW>(g, acc, slab, m0 + wm * WM, n0 + wn * WN, lane, M);
+  if (SPLITK) {
+    GemmArgs gs = g;   // split ks writes its partial product at C + ks * c_split_stride
+    gs.epi.crow.off += (int64_t)ks * g.c_split_stride;
+    store_tile<EPI, SM, SN, SW>(gs, acc, slab, m0 + wm * WM, n0 + wn * WN, lane, M);
+  } else {
+    store_tile<EPI, SM, SN, SW>(g, acc, slab, m0 + wm * WM, n0 + wn * WN, lane, M);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -716,8 +737,16 @@ static hipError_t launch_epi(GemmArgs g, int tile_cfg, hipStream_t stream) {
                        dim3(BIG_THREADS), 0, stream, g);
   } else if (tile_cfg == GEMM_TILE_256x256) {
     hipLaunchKernelGGL((gemm_bf16_256_kernel<EPI, false>), dim3(N_XCD * per_xcd), dim3(BIG_THREADS), 0, stream, g);
+  } else if (g.splits > 1) {
+    if constexpr (EPI == EPI_STORE_F32) {
+      const int per_xcd_all = (total * g.splits + N_XCD - 1) / N_XCD;
+      hipLaunchKernelGGL((gemm_bf16_128_kernel<EPI, true>), dim3(N_XCD * per_xcd_all), dim3(SMALL_THREADS), 0,
+                         stream, g);
+    } else {
+      return hipErrorInvalidValue;
+    }
   } else {
-    hipLaunchKernelGGL((gemm_bf16_128_kernel<EPI>), dim3(N_XCD * per_xcd), dim3(SMALL_THREADS), 0, stream, g);
+    hipLaunchKernelGGL((gemm_bf16_128_kernel<EPI, false>), dim3(N_XCD * per_xcd), dim3(SMALL_THREADS), 0, stream, g);
   }
   return hipGetLastError();
 }
@@ -752,6 +781,7 @@ hipError_t gemm_bf16(int epi, const bf16_t* A, RowMap arow, const bf16_t* W, int
   g.A = A; g.arow = arow; g.W = W; g.ldw = ldw; g.M = M; g.N = N; g.K = K; g.m_dev = m_dev; g.epi = ep;
   g.a_bytes = (uint32_t)(a_elems * 2);
   g.w_bytes = (uint32_t)(w_elems * 2);
+  g.splits = 1;
   switch (epi) {
     case EPI_STORE_BF16: return launch_epi<EPI_STORE_BF16>(g, tile_cfg, stream);
     case EPI_GELU_BF16: return launch_epi<EPI_GELU_BF16>(g, tile_cfg, stream);
@@ -761,6 +791,35 @@ hipError_t gemm_bf16(int epi, const bf16_t* A, RowMap arow, const bf16_t* W, int
     case EPI_QKV_BF16: return launch_epi<EPI_QKV_BF16>(g, tile_cfg, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+int gemm_residual_splits(int M, int N, int K) {
+  if (gemm_pick_tile(M, N) != GEMM_TILE_128x128) return 1;
+  const int64_t tiles = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
+  // two 128x128 workgroups per CU: below 384 tiles most of the 512 slots idle
+  if (tiles >= 384) return 1;
+  for (int s = 4; s >= 2; s /= 2)
+    if (tiles * s <= 1024 && (K / GEMM_BK) % s == 0 && K / s >= 4 * GEMM_BK) return s;
+  return 1;
+}
+
+hipError_t gemm_bf16_splitk(const bf16_t* A, RowMap arow, const bf16_t* W, int64_t ldw, int M, int N, int K,
+                            int splits, const int32_t* m_dev, float* parts, int64_t ldc, int64_t part_stride,
+                            hipStream_t stream) {
+  if (splits < 2 || K % (GEMM_BK * splits) != 0 || M <= 0 || N <= 0 || N % 4 != 0 || arow.map || !parts)
+    return hipErrorInvalidValue;
+  const int64_t a_elems = row_extent(arow, M, K), w_elems = (int64_t)(N - 1) * ldw + K;
+  if (a_elems * 2 >= (int64_t)UINT32_MAX || w_elems * 2 >= (int64_t)UINT32_MAX) return hipErrorInvalidValue;
+  if ((uint64_t)K * 2 * (splits - 1) >= UINT32_MAX) return hipErrorInvalidValue;
+  GemmArgs g{};
+  g.A = A; g.arow = arow; g.W = W; g.ldw = ldw; g.M = M; g.N = N; g.K = K / splits; g.m_dev = m_dev;
+  g.epi.c = parts;
+  g.epi.crow = dense_rows(ldc);
+  g.a_bytes = (uint32_t)(a_elems * 2);
+  g.w_bytes = (uint32_t)(w_elems * 2);
+  g.splits = splits;
+  g.c_split_stride = part_stride;
+  return launch_epi<EPI_STORE_F32>(g, GEMM_TILE_128x128, stream);
 }
 
 }  // namespace aenc

@@ -102,7 +102,8 @@ extern "C" int aenc_k_layernorm(const float* x, const float* gamma, const float*
                                 int d, float eps, void* stream) {
   if (!x || !gamma || !beta || !y) return fail("NULL operand");
   if (M < 1 || d < 4 || d % 4 || d > 2048 || (y_dtype != 0 && y_dtype != 1)) return fail("bad LayerNorm sizes");
-  return hip_status(layernorm(x, gamma, beta, y, y_dtype, M, nullptr, d, eps, (hipStream_t)stream), "layernorm");
+  return hip_status(layernorm(const_cast<float*>(x), gamma, beta, y, y_dtype, M, nullptr, d, eps, (hipStream_t)stream),
+                    "layernorm");
 }
 
 extern "C" int aenc_k_gelu_f32(const float* x, float* y, int64_t n, void* stream) {

@@ -15,6 +15,26 @@ hipError_t gemm_bf16(int epi, const bf16_t* A, RowMap arow, const bf16_t* W, int
 // The tile shape gemm_bf16 runs fastest with for an M x N output.
 int gemm_pick_tile(int M, int N);
 
+// Split-K for the residual products of short batches: gemm_residual_splits
+// gives the number of K ranges (1: none) worth launching for an M x N x K
+// product, gemm_bf16_splitk writes split s's partial product A[:, s K/S ..]
+// W[:, s K/S ..]^T (fp32, no bias) to parts + s * part_stride, rows ldc apart.
+// The consumer adds the partials, the bias and the residual (layernorm and
+// final_ln_out with ResidualParts).
+int gemm_residual_splits(int M, int N, int K);
+hipError_t gemm_bf16_splitk(const bf16_t* A, RowMap arow, const bf16_t* W, int64_t ldw, int M, int N, int K,
+                            int splits, const int32_t* m_dev, float* parts, int64_t ldc, int64_t part_stride,
+                            hipStream_t stream);
+
+// Partial products of a split residual product, folded into x by the next
+// normalisation: x[r] += bias + sum_s parts[s * stride + r * d] (n = 0: nothing).
+struct ResidualParts {
+  const float* parts;
+  int n;
+  int64_t stride;
+  const float* bias;
+};
+
 // fp32 GEMM on the vector ALUs (the fp32 path), same epilogues; K % 16 == 0.
 hipError_t gemm_f32(int epi, const float* A, RowMap arow, const float* W, int64_t ldw, int M, int N, int K,
                     const int32_t* m_dev, const EpiParams& ep, hipStream_t stream);
@@ -39,14 +59,17 @@ hipError_t attention_f32(const float* qkv, int64_t ld, const int32_t* start, con
                          const int32_t* key_hi, hipStream_t stream);
 
 // LayerNorm of fp32 rows: y[r] = LN(x[r]) for r < M (M = *m_dev if set).
-hipError_t layernorm(const float* x, const float* gamma, const float* beta, void* y, int y_dtype, int M,
-                     const int32_t* m_dev, int d, float eps, hipStream_t stream);
+// With rp.n > 0, x[r] first becomes x[r] + rp.bias + the partial rows (and is
+// written back): the residual update of a split product.
+hipError_t layernorm(float* x, const float* gamma, const float* beta, void* y, int y_dtype, int M,
+                     const int32_t* m_dev, int d, float eps, hipStream_t stream, ResidualParts rp = {});
 
 // Final LayerNorm written to the output layout [B, T_out, d]: output row (b, j)
 // reads packed row map[b*T + j] (pool 1) or the mean of LN rows map[b*T + 2j]
 // and map[b*T + 2j + 1] (pool 2); rows whose sources are masked become zeros.
 hipError_t final_ln_out(const float* x, const int32_t* map, const float* gamma, const float* beta, void* out,
-                        int out_dtype, int B, int T, int pool, int d, float eps, hipStream_t stream);
+                        int out_dtype, int B, int T, int pool, int d, float eps, hipStream_t stream,
+                        ResidualParts rp = {});
 
 // Zero the output rows of masked positions: out row i (of B*T) when map[i] < 0.
 hipError_t zero_masked_rows(const int32_t* map, void* out, int out_dtype, int rows, int width,

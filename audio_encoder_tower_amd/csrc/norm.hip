@@ -40,6 +40,24 @@ __device__ __forceinline__ void load_row(const float* x, float4 (&v)[LN_MAXV], i
     if (lane + 64 * i < n4) v[i] = ((const float4*)x)[lane + 64 * i];
 }
 
+__device__ __forceinline__ float4 add4(float4 a, float4 b) {
+  return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+}
+
+// The residual update of a split product: v (row `row` of x) += bias + every
+// partial row, in that order.
+__device__ __forceinline__ void fold_parts(float4 (&v)[LN_MAXV], const ResidualParts& rp, int64_t row, int d,
+                                           int n4, int lane) {
+#pragma unroll
+  for (int i = 0; i < LN_MAXV; ++i) {
+    const int j = lane + 64 * i;
+    if (j >= n4) continue;
+    float4 p = rp.bias ? ((const float4*)rp.bias)[j] : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s = 0; s < rp.n; ++s) p = add4(p, ((const float4*)(rp.parts + s * rp.stride + row * d))[j]);
+    v[i] = add4(v[i], p);
+  }
+}
+
 __device__ __forceinline__ float4 norm4(float4 x, const RowStats& st, float4 g, float4 b) {
   return make_float4((x.x - st.mean) * st.rstd * g.x + b.x, (x.y - st.mean) * st.rstd * g.y + b.y,
                      (x.z - st.mean) * st.rstd * g.z + b.z, (x.w - st.mean) * st.rstd * g.w + b.w);
@@ -53,16 +71,25 @@ __device__ __forceinline__ void store4(bf16_t* y, int j, float4 v) {
   ((u32x2*)y)[j] = w;
 }
 
-template <typename TO>
-__global__ __launch_bounds__(256) void layernorm_kernel(const float* __restrict__ x, const float* __restrict__ gamma,
+// PARTS: fold the partial products of a split residual product into x first
+// (and write x back).
+template <typename TO, bool PARTS>
+__global__ __launch_bounds__(256) void layernorm_kernel(float* __restrict__ x, const float* __restrict__ gamma,
                                                         const float* __restrict__ beta, TO* __restrict__ y,
-                                                        int M_arg, const int32_t* m_dev, int d, float eps) {
+                                                        int M_arg, const int32_t* m_dev, int d, float eps,
+                                                        ResidualParts rp) {
   const int M = m_dev ? *m_dev : M_arg;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= M) return;
   const int lane = threadIdx.x & 63, n4 = d >> 2;
   float4 v[LN_MAXV];
   load_row(x + (int64_t)row * d, v, n4, lane);
+  if (PARTS) {
+    fold_parts(v, rp, row, d, n4, lane);
+#pragma unroll
+    for (int i = 0; i < LN_MAXV; ++i)
+      if (lane + 64 * i < n4) ((float4*)(x + (int64_t)row * d))[lane + 64 * i] = v[i];
+  }
   const RowStats st = row_stats(v, n4, lane, d, eps);
   TO* yr = y + (int64_t)row * d;
 #pragma unroll
@@ -72,25 +99,31 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const float* __restrict_
   }
 }
 
-hipError_t layernorm(const float* x, const float* gamma, const float* beta, void* y, int y_dtype, int M,
-                     const int32_t* m_dev, int d, float eps, hipStream_t stream) {
-  if (d % 4 != 0 || d > 64 * 4 * LN_MAXV || M <= 0) return hipErrorInvalidValue;
+hipError_t layernorm(float* x, const float* gamma, const float* beta, void* y, int y_dtype, int M,
+                     const int32_t* m_dev, int d, float eps, hipStream_t stream, ResidualParts rp) {
+  if (d % 4 != 0 || d > 64 * 4 * LN_MAXV || M <= 0 || (rp.n > 0 && !rp.parts)) return hipErrorInvalidValue;
   dim3 grid((M + 3) / 4);
-  if (y_dtype == 1)
-    hipLaunchKernelGGL(layernorm_kernel<bf16_t>, grid, dim3(256), 0, stream, x, gamma, beta, (bf16_t*)y, M, m_dev,
-                       d, eps);
+  if (y_dtype == 1 && rp.n > 0)
+    hipLaunchKernelGGL((layernorm_kernel<bf16_t, true>), grid, dim3(256), 0, stream, x, gamma, beta, (bf16_t*)y, M,
+                       m_dev, d, eps, rp);
+  else if (y_dtype == 1)
+    hipLaunchKernelGGL((layernorm_kernel<bf16_t, false>), grid, dim3(256), 0, stream, x, gamma, beta, (bf16_t*)y, M,
+                       m_dev, d, eps, rp);
+  else if (rp.n > 0)
+    hipLaunchKernelGGL((layernorm_kernel<float, true>), grid, dim3(256), 0, stream, x, gamma, beta, (float*)y, M,
+                       m_dev, d, eps, rp);
   else
-    hipLaunchKernelGGL(layernorm_kernel<float>, grid, dim3(256), 0, stream, x, gamma, beta, (float*)y, M, m_dev, d,
-                       eps);
+    hipLaunchKernelGGL((layernorm_kernel<float, false>), grid, dim3(256), 0, stream, x, gamma, beta, (float*)y, M,
+                       m_dev, d, eps, rp);
   return hipGetLastError();
 }
 
 // Final LayerNorm into the output layout. Output row (b, j) of B*T_out.
-template <typename TO>
+template <typename TO, bool PARTS>
 __global__ __launch_bounds__(256) void final_ln_kernel(const float* __restrict__ x, const int32_t* __restrict__ map,
                                                        const float* __restrict__ gamma,
                                                        const float* __restrict__ beta, TO* __restrict__ out, int B,
-                                                       int T, int pool, int d, float eps) {
+                                                       int T, int pool, int d, float eps, ResidualParts rp) {
   const int t_out = T / pool;
   const int orow = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (orow >= B * t_out) return;
@@ -113,6 +146,7 @@ __global__ __launch_bounds__(256) void final_ln_kernel(const float* __restrict__
   for (int p = 0; p < pool; ++p) {
     float4 v[LN_MAXV];
     load_row(x + (int64_t)src[p] * d, v, n4, lane);
+    if (PARTS) fold_parts(v, rp, src[p], d, n4, lane);
     const RowStats st = row_stats(v, n4, lane, d, eps);
 #pragma unroll
     for (int i = 0; i < LN_MAXV; ++i) {
@@ -134,17 +168,25 @@ __global__ __launch_bounds__(256) void final_ln_kernel(const float* __restrict__
 }
 
 hipError_t final_ln_out(const float* x, const int32_t* map, const float* gamma, const float* beta, void* out,
-                        int out_dtype, int B, int T, int pool, int d, float eps, hipStream_t stream) {
-  if (d % 4 != 0 || d > 64 * 4 * LN_MAXV || (pool != 1 && pool != 2)) return hipErrorInvalidValue;
+                        int out_dtype, int B, int T, int pool, int d, float eps, hipStream_t stream,
+                        ResidualParts rp) {
+  if (d % 4 != 0 || d > 64 * 4 * LN_MAXV || (pool != 1 && pool != 2) || (rp.n > 0 && !rp.parts))
+    return hipErrorInvalidValue;
   const int rows = B * (T / pool);
   if (rows <= 0) return hipSuccess;
   dim3 grid((rows + 3) / 4);
-  if (out_dtype == 1)
-    hipLaunchKernelGGL(final_ln_kernel<bf16_t>, grid, dim3(256), 0, stream, x, map, gamma, beta, (bf16_t*)out, B, T,
-                       pool, d, eps);
+  if (out_dtype == 1 && rp.n > 0)
+    hipLaunchKernelGGL((final_ln_kernel<bf16_t, true>), grid, dim3(256), 0, stream, x, map, gamma, beta,
+                       (bf16_t*)out, B, T, pool, d, eps, rp);
+  else if (out_dtype == 1)
+    hipLaunchKernelGGL((final_ln_kernel<bf16_t, false>), grid, dim3(256), 0, stream, x, map, gamma, beta,
+                       (bf16_t*)out, B, T, pool, d, eps, rp);
+  else if (rp.n > 0)
+    hipLaunchKernelGGL((final_ln_kernel<float, true>), grid, dim3(256), 0, stream, x, map, gamma, beta, (float*)out,
+                       B, T, pool, d, eps, rp);
   else
-    hipLaunchKernelGGL(final_ln_kernel<float>, grid, dim3(256), 0, stream, x, map, gamma, beta, (float*)out, B, T,
-                       pool, d, eps);
+    hipLaunchKernelGGL((final_ln_kernel<float, false>), grid, dim3(256), 0, stream, x, map, gamma, beta, (float*)out,
+                       B, T, pool, d, eps, rp);
   return hipGetLastError();
 }
 

@@ -118,6 +118,7 @@ struct aenc_handle {
   struct Ws {
     void *melT, *g1, *a, *qk, *vt, *hmid;
     float* x;
+    float* parts;   // [parts][M_cap][d] fp32, or null
     int64_t ld_vt;
     // maps written per forward
     int32_t *row_map, *inv_map, *cu, *lens, *m_valid;
@@ -264,7 +265,8 @@ struct Layout {
   int T, T8, C_pad;
   int64_t M_cap, ld_vt;
   size_t esz;
-  size_t off_melT, off_g1, off_x, off_a, off_qk, off_vt, off_hmid, off_maps, total;
+  size_t off_melT, off_g1, off_x, off_a, off_qk, off_vt, off_hmid, off_parts, off_maps, total;
+  int parts;   // partial products of the split residual GEMMs (0: not split)
 };
 
 Layout workspace_layout(const aenc_geometry* g) {
@@ -287,6 +289,15 @@ Layout workspace_layout(const aenc_geometry* g) {
   L.off_qk = take(L.M_cap * (g->dtype == AENC_BF16 ? 2 : 3) * d * L.esz);
   L.off_vt = take(g->dtype == AENC_BF16 ? d * L.ld_vt * 2 : 0);
   L.off_hmid = take(L.M_cap * mid * L.esz);
+  // short bf16 batches split the residual products along K; the partials wait
+  // here for the next LayerNorm, which adds them to the residual stream
+  L.parts = 0;
+  if (g->dtype == AENC_BF16 && g->n_layers > 0) {
+    const int M_rows = (int)((int64_t)(B - 1) * L.T8 + L.T);
+    L.parts = std::max(gemm_residual_splits(M_rows, (int)d, (int)d), gemm_residual_splits(M_rows, (int)d, g->d_ffn));
+    if (L.parts < 2) L.parts = 0;
+  }
+  L.off_parts = take((size_t)L.parts * L.M_cap * d * 4);
   // row_map, inv_map, cu, lens, m_valid twice (per-forward and all-valid),
   // then the stacked-row maps twice when the projector reads stacked rows
   const int k = stack_of(g);
@@ -310,6 +321,7 @@ aenc_handle::Ws carve(const aenc_geometry* g, const Layout& L, int batch, char* 
   w.qk = base + L.off_qk;
   w.vt = base + L.off_vt;
   w.hmid = base + L.off_hmid;
+  w.parts = L.parts ? (float*)(base + L.off_parts) : nullptr;
   w.ld_vt = L.ld_vt;
   int32_t* maps = (int32_t*)(base + L.off_maps);
   const int64_t BT = (int64_t)batch * L.T;
@@ -755,10 +767,17 @@ int forward_impl(aenc_handle* h, const aenc_handle::Ws& w, int B, const void* me
   if (!q.done(K_CONV2, e, "conv2")) return AENC_E_HIP;
 
   const RowMap dense_d = dense_rows(d);
+  // Short batches split the residual products (O-proj, FC2) along K; the next
+  // LayerNorm adds the partials and the bias to the residual stream.
+  const int split_o = (bf && w.parts) ? gemm_residual_splits(M_rows, d, d) : 1;
+  const int split_f = (bf && w.parts) ? gemm_residual_splits(M_rows, d, f) : 1;
+  const int64_t part_stride = (int64_t)B * T8 * d;
+  ResidualParts pending{};   // partials the next LayerNorm folds in
   for (int l = 0; l < g.n_layers; ++l) {
     const aenc_handle::Layer& L = h->layers[l];
-    if (!q.done(K_LN, layernorm(w.x, L.ln1_g, L.ln1_b, w.a, g.dtype, M_rows, mv, d, g.ln_eps, s), "ln1"))
+    if (!q.done(K_LN, layernorm(w.x, L.ln1_g, L.ln1_b, w.a, g.dtype, M_rows, mv, d, g.ln_eps, s, pending), "ln1"))
       return AENC_E_HIP;
+    pending = ResidualParts{};
     EpiParams eq{};
     eq.bias = L.qkv_b;
     eq.c = w.qk;
@@ -784,17 +803,24 @@ int forward_impl(aenc_handle* h, const aenc_handle::Ws& w, int B, const void* me
       e = attention_f32((const float*)w.qk, 3 * d, cu, lens, B, T, g.n_heads, (float*)w.a, d, key_lo, key_hi, s);
     if (!q.done(K_ATTN, e, "attention")) return AENC_E_HIP;
 
-    EpiParams eo{};
-    eo.bias = L.o_b;
-    eo.c = w.x;
-    eo.crow = dense_d;
-    e = bf ? gemm_bf16(EPI_RESID_F32, (const bf16_t*)w.a, dense_d, (const bf16_t*)L.o_w, d, M_rows, d, d, mv, eo,
-                       pick_tile(M_rows, d), s)
-           : gemm_f32(EPI_RESID_F32, (const float*)w.a, dense_d, (const float*)L.o_w, d, M_rows, d, d, mv, eo, s);
+    if (split_o > 1) {
+      e = gemm_bf16_splitk((const bf16_t*)w.a, dense_d, (const bf16_t*)L.o_w, d, M_rows, d, d, split_o, mv, w.parts,
+                           d, part_stride, s);
+      pending = ResidualParts{w.parts, split_o, part_stride, L.o_b};
+    } else {
+      EpiParams eo{};
+      eo.bias = L.o_b;
+      eo.c = w.x;
+      eo.crow = dense_d;
+      e = bf ? gemm_bf16(EPI_RESID_F32, (const bf16_t*)w.a, dense_d, (const bf16_t*)L.o_w, d, M_rows, d, d, mv, eo,
+                         pick_tile(M_rows, d), s)
+             : gemm_f32(EPI_RESID_F32, (const float*)w.a, dense_d, (const float*)L.o_w, d, M_rows, d, d, mv, eo, s);
+    }
     if (!q.done(K_OPROJ, e, "o_proj")) return AENC_E_HIP;
 
-    if (!q.done(K_LN, layernorm(w.x, L.ln2_g, L.ln2_b, w.a, g.dtype, M_rows, mv, d, g.ln_eps, s), "ln2"))
+    if (!q.done(K_LN, layernorm(w.x, L.ln2_g, L.ln2_b, w.a, g.dtype, M_rows, mv, d, g.ln_eps, s, pending), "ln2"))
       return AENC_E_HIP;
+    pending = ResidualParts{};
 
     EpiParams ef1{};
     ef1.bias = L.fc1_b;
@@ -805,26 +831,33 @@ int forward_impl(aenc_handle* h, const aenc_handle::Ws& w, int B, const void* me
            : gemm_f32(EPI_GELU_F32, (const float*)w.a, dense_d, (const float*)L.fc1_w, d, M_rows, f, d, mv, ef1, s);
     if (!q.done(K_FC1, e, "fc1")) return AENC_E_HIP;
 
-    EpiParams ef2{};
-    ef2.bias = L.fc2_b;
-    ef2.c = w.x;
-    ef2.crow = dense_d;
-    e = bf ? gemm_bf16(EPI_RESID_F32, (const bf16_t*)w.hmid, dense_rows(f), (const bf16_t*)L.fc2_w, f, M_rows, d, f,
-                       mv, ef2, pick_tile(M_rows, d), s)
-           : gemm_f32(EPI_RESID_F32, (const float*)w.hmid, dense_rows(f), (const float*)L.fc2_w, f, M_rows, d, f, mv,
-                      ef2, s);
+    if (split_f > 1) {
+      e = gemm_bf16_splitk((const bf16_t*)w.hmid, dense_rows(f), (const bf16_t*)L.fc2_w, f, M_rows, d, f, split_f,
+                           mv, w.parts, d, part_stride, s);
+      pending = ResidualParts{w.parts, split_f, part_stride, L.fc2_b};
+    } else {
+      EpiParams ef2{};
+      ef2.bias = L.fc2_b;
+      ef2.c = w.x;
+      ef2.crow = dense_d;
+      e = bf ? gemm_bf16(EPI_RESID_F32, (const bf16_t*)w.hmid, dense_rows(f), (const bf16_t*)L.fc2_w, f, M_rows, d,
+                         f, mv, ef2, pick_tile(M_rows, d), s)
+             : gemm_f32(EPI_RESID_F32, (const float*)w.hmid, dense_rows(f), (const float*)L.fc2_w, f, M_rows, d, f,
+                        mv, ef2, s);
+    }
     if (!q.done(K_FC2, e, "fc2")) return AENC_E_HIP;
   }
 
   if (!g.proj_hidden) {
     if (!q.done(K_FINAL, final_ln_out(w.x, row_map, h->lnf_g, h->lnf_b, out, g.out_dtype, B, T, g.pool_step, d,
-                                      g.ln_eps, s), "final ln"))
+                                      g.ln_eps, s, pending), "final ln"))
       return AENC_E_HIP;
     return AENC_OK;
   }
 
   const int ph = g.proj_hidden, po = g.proj_out;
-  if (!q.done(K_FINAL, layernorm(w.x, h->lnf_g, h->lnf_b, w.a, g.dtype, M_rows, mv, d, g.ln_eps, s), "final ln"))
+  if (!q.done(K_FINAL, layernorm(w.x, h->lnf_g, h->lnf_b, w.a, g.dtype, M_rows, mv, d, g.ln_eps, s, pending),
+              "final ln"))
     return AENC_E_HIP;
   // Projector rows: the packed LN rows themselves, or (stack k) runs of k
   // packed rows read as one k*d-wide row. Clip starts are multiples of 8, so

@@ -214,11 +214,12 @@ int aenc_handle_geometry(const aenc_handle *h, aenc_geometry *g);
  * range, or a workspace for n_clips clips over AENC_NOALLOC_SCRATCH_BYTES:
  * aenc_last_error() gives the size needed) or AENC_E_HIP (launch failure).
  * A Whisper-large clip (3000 frames, d_model 1280, FFN 5120) needs about
- * 47 MB, so the array holds one such clip per call.
+ * 78 MB (its residual products are split along K, whose partials take 31 MB),
+ * so the array holds one such clip per call.
  *
  * aenc_noalloc_scratch_bytes: the bytes n_clips clips of g need in the array
  * (host only; -1 for an invalid geometry or n_clips outside 1..g->batch). */
-#define AENC_NOALLOC_SCRATCH_BYTES (64LL << 20)
+#define AENC_NOALLOC_SCRATCH_BYTES (96LL << 20)
 int aenc_forward_noalloc(aenc_handle *h, int n_clips, const void *mel, const uint8_t *mask, void *out,
                          void *stream);
 int64_t aenc_noalloc_scratch_bytes(const aenc_geometry *g, int n_clips);

@@ -95,18 +95,19 @@ def test_noalloc_matches_the_forward_on_two_calls(aenc):
 
 def test_noalloc_rejects_what_does_not_fit(aenc):
     w = synth.get_workload("whisper_large_b1")
-    g = w.geom.replace(batch=2, n_layers=0)
-    need1 = aenc.lib().aenc_noalloc_scratch_bytes(ctypes.byref(aenc._lib.geometry(g)), 1)
-    need2 = aenc.lib().aenc_noalloc_scratch_bytes(ctypes.byref(aenc._lib.geometry(g)), 2)
-    assert 0 < need1 <= aenc._lib.AENC_NOALLOC_SCRATCH_BYTES < need2
+    g = w.geom.replace(batch=3, n_layers=1)
+    cg = ctypes.byref(aenc._lib.geometry(g))
+    L = aenc.lib()
+    need = [L.aenc_noalloc_scratch_bytes(cg, n) for n in (1, 2, 3)]
+    assert 0 < need[0] <= aenc._lib.AENC_NOALLOC_SCRATCH_BYTES < need[1] < need[2]
+    assert L.aenc_noalloc_scratch_bytes(cg, 0) == -1 and L.aenc_noalloc_scratch_bytes(cg, 4) == -1
     W = synth.make_weights(w.replace(geom=g))
     enc = _encoder(aenc, w.replace(geom=g), W)
-    mel = torch.zeros(2, g.n_mel, g.n_frames, device=DEV, dtype=torch.bfloat16)
+    mel = torch.zeros(3, g.n_mel, g.n_frames, device=DEV, dtype=torch.bfloat16)
     out = torch.zeros(enc.out_shape, device=DEV, dtype=enc.out_dtype)
-    L = aenc.lib()
     assert L.aenc_forward_noalloc(enc._h, 2, _p(mel), None, _p(out), _stream()) == -1
     assert "scratch" in aenc.last_error()
-    assert L.aenc_forward_noalloc(enc._h, 3, _p(mel), None, _p(out), _stream()) == -1
+    assert L.aenc_forward_noalloc(enc._h, 4, _p(mel), None, _p(out), _stream()) == -1
     assert L.aenc_forward_noalloc(enc._h, 0, _p(mel), None, _p(out), _stream()) == -1
     assert L.aenc_forward_noalloc(None, 1, _p(mel), None, _p(out), _stream()) == -1
     assert L.aenc_forward_noalloc(enc._h, 1, None, None, _p(out), _stream()) == -1
