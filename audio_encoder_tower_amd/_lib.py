@@ -10,7 +10,9 @@ import os
 from ctypes import POINTER, c_char_p, c_double, c_float, c_int, c_int32, c_int64, c_void_p
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libaenc.so")
+# AENC_LIBRARY may name another build of the same library (the host-sanitizer
+# copy that `python -m audio_encoder_tower_amd.build --sanitize` writes).
+LIB_PATH = os.environ.get("AENC_LIBRARY") or os.path.join(PKG, "libaenc.so")
 
 AENC_F32 = 0
 AENC_BF16 = 1
