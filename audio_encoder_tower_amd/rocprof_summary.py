@@ -1,8 +1,14 @@
 """Summaries of rocprofv3 CSV output for the encoder's kernels.
 
 Usage:
-  python -m audio_encoder_tower_amd.rocprof_summary trace <dir>     kernel trace (--kernel-trace --stats)
-  python -m audio_encoder_tower_amd.rocprof_summary counters <dir>  counter runs (--pmc ...)
+  python -m audio_encoder_tower_amd.rocprof_summary trace <dir> [--cycle KERNEL=a,b ...]
+  python -m audio_encoder_tower_amd.rocprof_summary counters <dir> [--cycle KERNEL=a,b ...]
+
+  trace: a kernel-trace run (--kernel-trace --stats); counters: a --pmc run.
+  --cycle labels the dispatches of one kernel (its short name, e.g.
+  "gemm_bf16_256_kernel<2, false>") in dispatch order with the given labels in
+  turn, so that two steps that run the same kernel at the same grid (the
+  O-projection and FC2 of every block) are reported apart.
 
 <dir> is the -d directory of a rocprofv3 run with --output-format csv; the
 files found under it (*kernel_trace.csv, *counter_collection.csv) are read.
@@ -34,18 +40,40 @@ def _files(d: str, suffix: str):
 
 def _short(name: str) -> str:
     name = name.replace("aenc::", "").replace("(anonymous namespace)::", "")
+    if name.startswith("void "):
+        name = name[5:]
     i = name.find("(")
     return name[:i] if i > 0 else name
 
 
-def trace(d: str) -> str:
+def _labeler(cycles):
+    """(short kernel name) -> labels assigned in turn to its dispatches."""
+    seen = collections.Counter()
+
+    def label(name: str, grid: int):
+        labels = cycles.get(name)
+        if not labels:
+            return name, grid
+        i = seen[(name, grid)]
+        seen[(name, grid)] += 1
+        return f"{name} [{labels[i % len(labels)]}]", grid
+    return label
+
+
+def _rows(f: str):
+    with open(f) as fh:
+        rows = list(csv.DictReader(fh))
+    return sorted(rows, key=lambda r: int(r.get("Dispatch_Id", r.get("Correlation_Id", 0)) or 0))
+
+
+def trace(d: str, cycles=None) -> str:
     groups = collections.OrderedDict()
+    label = _labeler(cycles or {})
     for f in _files(d, "kernel_trace.csv"):
-        with open(f) as fh:
-            for r in csv.DictReader(fh):
-                key = (_short(r["Kernel_Name"]), int(r.get("Grid_Size", r.get("Grid_Size_X", 0)) or 0))
-                dt = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-6
-                groups.setdefault(key, []).append(dt)
+        for r in _rows(f):
+            key = label(_short(r["Kernel_Name"]), int(r.get("Grid_Size", r.get("Grid_Size_X", 0)) or 0))
+            dt = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-6
+            groups.setdefault(key, []).append(dt)
     total = sum(sum(v) for v in groups.values()) or 1.0
     out = ["| kernel | grid | calls | avg ms | min ms | max ms | share |", "|---|---|---|---|---|---|---|"]
     for (k, g), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
@@ -63,16 +91,20 @@ def _n_xcc(d: str) -> int:
     return 8
 
 
-def counters(d: str) -> str:
+def counters(d: str, cycles=None) -> str:
     # (kernel, grid) -> dispatch -> counter -> value (rocprofv3 writes one row
     # per dispatch and counter, already summed over the counter's instances)
     per = collections.OrderedDict()
     dur = collections.defaultdict(dict)
+    label = _labeler(cycles or {})
     for f in _files(d, "counter_collection.csv"):
-        with open(f) as fh:
-            for r in csv.DictReader(fh):
-                key = (_short(r["Kernel_Name"]), int(r.get("Grid_Size", 0) or 0))
-                disp = (f, r.get("Dispatch_Id", r.get("Correlation_Id")))
+        keys = {}
+        for r in _rows(f):
+            disp = (f, r.get("Dispatch_Id", r.get("Correlation_Id")))
+            if disp not in keys:
+                keys[disp] = label(_short(r["Kernel_Name"]), int(r.get("Grid_Size", 0) or 0))
+            key = keys[disp]
+            if True:  # noqa: SIM108 (one row per dispatch and counter)
                 per.setdefault(key, collections.OrderedDict()).setdefault(disp, {})[r["Counter_Name"]] = \
                     float(r["Counter_Value"])
                 if r.get("End_Timestamp") and r.get("Start_Timestamp"):
@@ -105,9 +137,17 @@ def counters(d: str) -> str:
 
 
 def main(argv):
-    if len(argv) != 3 or argv[1] not in ("trace", "counters"):
+    if len(argv) < 3 or argv[1] not in ("trace", "counters"):
         sys.exit(__doc__)
-    print(trace(argv[2]) if argv[1] == "trace" else counters(argv[2]))
+    cycles = {}
+    rest = argv[3:]
+    while rest:
+        if rest[0] != "--cycle" or len(rest) < 2 or "=" not in rest[1]:
+            sys.exit(__doc__)
+        name, labels = rest[1].rsplit("=", 1)
+        cycles[name] = labels.split(",")
+        rest = rest[2:]
+    print(trace(argv[2], cycles) if argv[1] == "trace" else counters(argv[2], cycles))
 
 
 if __name__ == "__main__":

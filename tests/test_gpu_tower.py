@@ -127,6 +127,9 @@ REDUCED = {
     "projector_one_position": reduced("whisper_large_b1", "projector_one_position",
                                       dict(n_layers=1, n_frames=2, proj_hidden=3072, proj_out=3072),
                                       init="perturbed"),
+    # a long masked batch on the 256x256 tiles: the device row count (12 clips, several short) leaves
+    # 190 tiles of valid rows of the 355 the launch is sized for, split evenly over the XCDs
+    "batch12_masked": reduced("whisper_large_b1", "batch12_masked", dict(batch=12, n_layers=1), init="perturbed"),
 }
 
 
@@ -140,6 +143,7 @@ LENGTHS = {
     "chunk_causal_masked": [900, 433, 97],
     "empty_clip_masked": [400, 0, 51],
     "fp32_chunk_causal_masked": [200, 137, 61],
+    "batch12_masked": [3000, 2999, 1700, 900, 401, 3000, 100, 2000, 1200, 800, 3000, 57],
 }
 
 
