@@ -63,6 +63,9 @@ struct GemmArgs {
   // its partial product (EPI_STORE_F32, no bias) at C offset s * c_split_stride.
   int splits;
   int64_t c_split_stride;
+  // the device row count may be well below M (a masked batch): let the
+  // workgroups decide the split tail from it
+  bool rows_vary;
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -731,7 +734,7 @@ static hipError_t launch_epi(GemmArgs g, int tile_cfg, hipStream_t stream) {
   // sized for g.M rows; a device row count below it leaves workgroups idle
   const int total = (g.M + bt - 1) / bt * g.tiles_n;
   const int per_xcd = (total + N_XCD - 1) / N_XCD;
-  if (tile_cfg == GEMM_TILE_256x256 && split_pays(total)) {
+  if (tile_cfg == GEMM_TILE_256x256 && (split_pays(total) || g.rows_vary)) {
     // a split XCD runs at most 16 extra half-tile workgroups
     hipLaunchKernelGGL((gemm_bf16_256_kernel<EPI, true>), dim3(N_XCD * (per_xcd + CUS_PER_XCD / 2)),
                        dim3(BIG_THREADS), 0, stream, g);
@@ -766,7 +769,7 @@ static int64_t row_extent(const RowMap& r, int M, int K) {
 }
 
 hipError_t gemm_bf16(int epi, const bf16_t* A, RowMap arow, const bf16_t* W, int64_t ldw, int M, int N, int K,
-                     const int32_t* m_dev, const EpiParams& ep, int tile_cfg, hipStream_t stream) {
+                     const int32_t* m_dev, const EpiParams& ep, int tile_cfg, hipStream_t stream, bool rows_vary) {
   // K in whole slices; N in groups of 4 (the epilogue writes 4 columns per lane).
   if (K % GEMM_BK != 0 || M <= 0 || N <= 0 || N % 4 != 0) return hipErrorInvalidValue;
   if (tile_cfg != GEMM_TILE_256x256 && tile_cfg != GEMM_TILE_128x128) return hipErrorInvalidValue;
@@ -782,6 +785,7 @@ hipError_t gemm_bf16(int epi, const bf16_t* A, RowMap arow, const bf16_t* W, int
   g.a_bytes = (uint32_t)(a_elems * 2);
   g.w_bytes = (uint32_t)(w_elems * 2);
   g.splits = 1;
+  g.rows_vary = rows_vary && m_dev;
   switch (epi) {
     case EPI_STORE_BF16: return launch_epi<EPI_STORE_BF16>(g, tile_cfg, stream);
     case EPI_GELU_BF16: return launch_epi<EPI_GELU_BF16>(g, tile_cfg, stream);

@@ -8,9 +8,12 @@ namespace aenc {
 
 enum GemmTile { GEMM_TILE_256x256 = 0, GEMM_TILE_128x128 = 1 };
 
-// bf16 MFMA GEMM, C = epi(A W^T + b); K % 64 == 0.
+// bf16 MFMA GEMM, C = epi(A W^T + b); K % 64 == 0. rows_vary: *m_dev may be
+// well below M (a masked batch), so the split of the last round of tiles is
+// decided on the device from it.
 hipError_t gemm_bf16(int epi, const bf16_t* A, RowMap arow, const bf16_t* W, int64_t ldw, int M, int N, int K,
-                     const int32_t* m_dev, const EpiParams& ep, int tile_cfg, hipStream_t stream);
+                     const int32_t* m_dev, const EpiParams& ep, int tile_cfg, hipStream_t stream,
+                     bool rows_vary = false);
 
 // The tile shape gemm_bf16 runs fastest with for an M x N output.
 int gemm_pick_tile(int M, int N);

@@ -728,8 +728,10 @@ int forward_impl(aenc_handle* h, const aenc_handle::Ws& w, int B, const void* me
       key_lo = w.key_lo; key_hi = w.key_hi;
     }
   }
-  // Rows of the packed layout the GEMMs must cover at most (all clips full).
+  // Rows of the packed layout the GEMMs must cover at most (all clips full);
+  // under a mask the valid rows (on the device) may be far fewer
   const int M_rows = (int)((int64_t)(B - 1) * T8 + T);
+  const bool vary = mask != nullptr;
 
   if (!q.done(K_MEL, mel_transpose(mel, g.dtype, w.melT, B, C, h->C_pad, F, w.g1, g.dtype, d, s), "mel transpose"))
     return AENC_E_HIP;
@@ -789,7 +791,7 @@ int forward_impl(aenc_handle* h, const aenc_handle::Ws& w, int B, const void* me
       eq.q_cols = d;                 // the attention kernel takes Q in base-2 score units
       eq.q_scale = ATT_Q_SCALE;
       e = gemm_bf16(EPI_QKV_BF16, (const bf16_t*)w.a, dense_d, (const bf16_t*)L.qkv_w, d, M_rows, 3 * d, d, mv, eq,
-                    pick_tile(M_rows, 3 * d), s);
+                    pick_tile(M_rows, 3 * d), s, vary);
     } else {
       eq.crow = dense_rows(3 * d);
       e = gemm_f32(EPI_STORE_F32, (const float*)w.a, dense_d, (const float*)L.qkv_w, d, M_rows, 3 * d, d, mv, eq, s);
@@ -813,7 +815,7 @@ int forward_impl(aenc_handle* h, const aenc_handle::Ws& w, int B, const void* me
       eo.c = w.x;
       eo.crow = dense_d;
       e = bf ? gemm_bf16(EPI_RESID_F32, (const bf16_t*)w.a, dense_d, (const bf16_t*)L.o_w, d, M_rows, d, d, mv, eo,
-                         pick_tile(M_rows, d), s)
+                         pick_tile(M_rows, d), s, vary)
              : gemm_f32(EPI_RESID_F32, (const float*)w.a, dense_d, (const float*)L.o_w, d, M_rows, d, d, mv, eo, s);
     }
     if (!q.done(K_OPROJ, e, "o_proj")) return AENC_E_HIP;
@@ -827,7 +829,7 @@ int forward_impl(aenc_handle* h, const aenc_handle::Ws& w, int B, const void* me
     ef1.c = w.hmid;
     ef1.crow = dense_rows(f);
     e = bf ? gemm_bf16(EPI_GELU_BF16, (const bf16_t*)w.a, dense_d, (const bf16_t*)L.fc1_w, d, M_rows, f, d, mv, ef1,
-                       pick_tile(M_rows, f), s)
+                       pick_tile(M_rows, f), s, vary)
            : gemm_f32(EPI_GELU_F32, (const float*)w.a, dense_d, (const float*)L.fc1_w, d, M_rows, f, d, mv, ef1, s);
     if (!q.done(K_FC1, e, "fc1")) return AENC_E_HIP;
 
@@ -841,7 +843,7 @@ int forward_impl(aenc_handle* h, const aenc_handle::Ws& w, int B, const void* me
       ef2.c = w.x;
       ef2.crow = dense_d;
       e = bf ? gemm_bf16(EPI_RESID_F32, (const bf16_t*)w.hmid, dense_rows(f), (const bf16_t*)L.fc2_w, f, M_rows, d,
-                         f, mv, ef2, pick_tile(M_rows, d), s)
+                         f, mv, ef2, pick_tile(M_rows, d), s, vary)
              : gemm_f32(EPI_RESID_F32, (const float*)w.hmid, dense_rows(f), (const float*)L.fc2_w, f, M_rows, d, f,
                         mv, ef2, s);
     }
