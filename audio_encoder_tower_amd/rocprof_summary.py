@@ -3,12 +3,20 @@
 Usage:
   python -m audio_encoder_tower_amd.rocprof_summary trace <dir> [--cycle KERNEL=a,b ...]
   python -m audio_encoder_tower_amd.rocprof_summary counters <dir> [--cycle KERNEL=a,b ...]
+  python -m audio_encoder_tower_amd.rocprof_summary traffic <fetch dir> <write dir> --copy-mib MIB \
+      --step STEP=KERNEL@GRID ... [--cycle KERNEL=a,b ...]
 
   trace: a kernel-trace run (--kernel-trace --stats); counters: a --pmc run.
   --cycle labels the dispatches of one kernel (its short name, e.g.
   "gemm_bf16_256_kernel<2, false>") in dispatch order with the given labels in
   turn, so that two steps that run the same kernel at the same grid (the
   O-projection and FC2 of every block) are reported apart.
+  traffic: HBM bytes per launch of the named steps from a FETCH_SIZE run and a
+  WRITE_SIZE run of the same program, each run having first passed MIB MiB
+  through the plain copy kernel (bench.py --copy-probe-mib): each counter is
+  scaled by what it reads for that copy (MIB MiB each way). Prints JSON with
+  a digest of each step's kernel sources, so readings taken on other sources
+  can be told apart.
 
 <dir> is the -d directory of a rocprofv3 run with --output-format csv; the
 files found under it (*kernel_trace.csv, *counter_collection.csv) are read.
@@ -27,11 +35,31 @@ from __future__ import annotations
 import collections
 import csv
 import glob
+import hashlib
+import json
 import os
 import sys
 
 N_CU = 256
 N_SIMD = 4 * N_CU
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+
+# Kernel sources whose change invalidates stored hardware-counter readings.
+KERNEL_SOURCES = {
+    kind: ["gemm_bf16.hip", "epilogue.h", "common.h", "launch.h"]
+    for kind in ("qkv", "o_proj", "fc1", "fc2", "proj1", "proj2", "conv1", "conv2")
+}
+KERNEL_SOURCES["attention"] = ["attention.hip", "common.h", "launch.h"]
+KERNEL_SOURCES["layernorm"] = ["norm.hip", "common.h", "launch.h"]
+KERNEL_SOURCES["final_ln"] = ["norm.hip", "common.h", "launch.h"]
+
+
+def source_digest(kind: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES.get(kind, []):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def _files(d: str, suffix: str):
@@ -136,18 +164,75 @@ def counters(d: str, cycles=None) -> str:
     return "\n".join(out)
 
 
+def _counter_avgs(d: str, counter: str, cycles=None):
+    """(labelled kernel, grid) -> (dispatches, average value of `counter`)."""
+    per = collections.defaultdict(list)
+    label = _labeler(cycles or {})
+    for f in _files(d, "counter_collection.csv"):
+        for r in _rows(f):
+            if r["Counter_Name"] == counter:
+                per[label(_short(r["Kernel_Name"]), int(r.get("Grid_Size", 0) or 0))].append(
+                    float(r["Counter_Value"]))
+    return {k: (len(v), sum(v) / len(v)) for k, v in per.items()}
+
+
+def traffic(fetch_dir: str, write_dir: str, copy_mib: float, steps, cycles=None) -> str:
+    fetch = _counter_avgs(fetch_dir, "FETCH_SIZE", cycles)
+    write = _counter_avgs(write_dir, "WRITE_SIZE", cycles)
+    moved_kib = copy_mib * 1024.0
+    # the copy kernel's one dispatch of copy_mib MiB (its largest grid)
+    copies = [k for k in fetch if k[0] == "copy_kernel"]
+    if not copies:
+        sys.exit("no copy_kernel dispatch in the FETCH_SIZE run (run with --copy-probe-mib)")
+    ck = max(copies, key=lambda k: k[1])
+    f_scale = moved_kib / fetch[ck][1]
+    w_scale = moved_kib / write[ck][1]
+    out = {"about": ("HBM-side bytes per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch), "
+                     f"each scaled by what the counter reads for the plain copy kernel over {copy_mib:g} MiB "
+                     "in the same run"),
+           "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4), "kernels": {}}
+    for step, (kernel, grid) in steps.items():
+        keys = [k for k in fetch if k[0] == kernel and k[1] == grid]
+        if not keys or keys[0] not in write:
+            sys.exit(f"no dispatch of {kernel} at grid {grid} in both runs")
+        k = keys[0]
+        fk, wk = fetch[k][1], write[k][1]
+        out["kernels"][step] = {
+            "kernel": kernel, "grid": grid, "fetch_kib_raw": round(fk, 1), "write_kib_raw": round(wk, 1),
+            "fetch_bytes": round(fk * f_scale * 1024), "write_bytes": round(wk * w_scale * 1024),
+            "bytes_per_launch": round((fk * f_scale + wk * w_scale) * 1024),
+            "dispatches": [fetch[k][0], write[k][0]], "source_digest": source_digest(step)}
+    return json.dumps(out, indent=1)
+
+
 def main(argv):
-    if len(argv) < 3 or argv[1] not in ("trace", "counters"):
+    if len(argv) < 3 or argv[1] not in ("trace", "counters", "traffic"):
         sys.exit(__doc__)
-    cycles = {}
-    rest = argv[3:]
+    cycles, steps, copy_mib = {}, {}, None
+    rest = argv[3:] if argv[1] != "traffic" else argv[4:]
     while rest:
-        if rest[0] != "--cycle" or len(rest) < 2 or "=" not in rest[1]:
+        if len(rest) < 2:
             sys.exit(__doc__)
-        name, labels = rest[1].rsplit("=", 1)
-        cycles[name] = labels.split(",")
+        if rest[0] == "--cycle" and "=" in rest[1]:
+            name, labels = rest[1].rsplit("=", 1)
+            cycles[name] = labels.split(",")
+        elif rest[0] == "--step" and "=" in rest[1] and "@" in rest[1]:
+            step, spec = rest[1].split("=", 1)
+            kernel, grid = spec.rsplit("@", 1)
+            steps[step] = (kernel, int(grid))
+        elif rest[0] == "--copy-mib":
+            copy_mib = float(rest[1])
+        else:
+            sys.exit(__doc__)
         rest = rest[2:]
-    print(trace(argv[2], cycles) if argv[1] == "trace" else counters(argv[2], cycles))
+    if argv[1] == "trace":
+        print(trace(argv[2], cycles))
+    elif argv[1] == "counters":
+        print(counters(argv[2], cycles))
+    else:
+        if len(argv) < 4 or copy_mib is None or not steps:
+            sys.exit(__doc__)
+        print(traffic(argv[2], argv[3], copy_mib, steps, cycles))
 
 
 if __name__ == "__main__":

@@ -126,23 +126,6 @@ def oracle_flops(w, clips: int) -> float:
     return oracle.flops(w.geom.replace(batch=clips), synth.make_lengths(w, clips))
 
 
-# Kernel sources whose change invalidates stored hardware-counter readings.
-KERNEL_SOURCES = {
-    kind: ["gemm_bf16.hip", "epilogue.h", "common.h", "launch.h"]
-    for kind in ("qkv", "o_proj", "fc1", "fc2", "proj1", "proj2")
-}
-KERNEL_SOURCES["attention"] = ["attention.hip", "common.h", "launch.h"]
-
-
-def source_digest(kind: str) -> str:
-    import hashlib
-    h = hashlib.sha256()
-    for f in KERNEL_SOURCES.get(kind, []):
-        with open(os.path.join(ROOT, "audio_encoder_tower_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
-
-
 def measured_traffic(kind: str):
     """HBM bytes per launch of `kind` from profiles/traffic.json (rocprofv3
     FETCH_SIZE and WRITE_SIZE, scaled by the plain copy kernel's reading), or
@@ -152,6 +135,7 @@ def measured_traffic(kind: str):
         return None
     with open(path) as f:
         data = json.load(f)
+    from audio_encoder_tower_amd.rocprof_summary import source_digest
     entry = data.get("kernels", {}).get(kind)
     if not entry or entry.get("source_digest") != source_digest(kind):
         return None
@@ -555,6 +539,10 @@ def main():
         if k == "layernorm":   # fp32 rows in, bf16 (or fp32) rows out
             nbytes = rows * g.d_model * (4 + (2 if g.dtype == "bf16" else 4))
             entry["gbs"] = round(nbytes / (avg * 1e-3) / 1e9, 1)
+        if w.name == synth.workloads.HEADLINE:
+            t = measured_traffic(k)   # counter bytes per launch, taken on this workload
+            if t:
+                entry["counter_bytes_per_launch"] = t
         per_kind[k] = entry
     dominant = max(kinds, key=lambda k: kinds[k][0])
     dom_ms, dom_n = kinds[dominant]
