@@ -14,10 +14,12 @@
 //   - 64-key tiles of K (row-major) and V (already transposed by the QKV
 //     GEMM's epilogue) are staged in LDS, double-buffered through registers;
 //   - S^T = K Q^T on v_mfma_f32_32x32x16_bf16, so each lane holds 32 scores of
-//     a single query (its partner lane l^32 holds the other 32): the row max
-//     and row sum need one cross-lane exchange per tile, not a tree;
+//     a single query (its partner lane l^32 holds the other 32): the row sum
+//     needs one cross-lane exchange at the end, the row max one only when the
+//     reference maximum moves (below);
 //   - P^T in registers is exactly the B operand of O^T = V^T P^T, so P never
-//     goes through LDS; V^T's keys are stored in the order that matches;
+//     goes through LDS: K rows are placed in LDS so that each lane's scores
+//     cover runs of 8 consecutive keys, and V^T tiles are stored as loaded;
 //   - Q arrives pre-scaled by log2(e)/sqrt(64) (the QKV epilogue applies it
 //     before rounding), and each tile's score accumulator starts at minus the
 //     row's reference maximum, so the MFMAs yield base-2 exponents ready for
@@ -43,6 +45,14 @@ constexpr int ATT_D = 64;
 // cycle from 64 banks (two rows), so chunk c of row r sits at c ^ ((r/2) mod 8)
 // and 16 consecutive rows reading the same chunk use 16 distinct bank groups.
 __device__ __forceinline__ int att_swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
+
+// K rows sit in LDS with bits 2 and 3 of the key index swapped (an involution:
+// LDS row r holds key key_row(r)). The score MFMA gives lane half hh the rows
+// 8a + 4hh + (0..3) of each 32-row block; through the swap those are keys
+// 16(a/2) + 8hh + 4(a%2) + (0..3), so each lane half holds runs of 8
+// consecutive keys: exactly the K-index order in which the P V MFMA takes its
+// B operand, with V^T's keys in their natural order.
+__device__ __forceinline__ int key_row(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
 
 // RANGED: query row r (clip-relative index i) sees only the clip's keys
 // [key_lo[r], key_hi[r]), non-empty and non-decreasing in i (the chunk rules);
@@ -164,17 +174,12 @@ __global__ __launch_bounds__(64 * NW) void attention_bf16_kernel(const bf16_t* _
     for (int i = 0; i < CH; ++i) {
       const int c = tid + THREADS * i;
       const int key = c >> 3, ch = c & 7;
-      *(u32x4*)(&Ks[buf][key * ATT_D + att_swz(key, ch) * 8]) = rk[i];
-      // Keys 8kc .. 8kc+7 are two groups of four; within each 16-key block the
-      // groups are stored in the order (0, 2, 1, 3) so that lane half 0 reads
-      // keys {0-3, 8-11} and lane half 1 reads {4-7, 12-15} as one 16-byte chunk.
+      // K row `key` goes to LDS row key_row(key) (bits 2 and 3 of the key
+      // swapped; see tile), V^T chunks to their own places
+      const int kr = key_row(key);
+      *(u32x4*)(&Ks[buf][kr * ATT_D + att_swz(kr, ch) * 8]) = rk[i];
       const int e = c >> 3, kc = c & 7;
-      const int blk = 16 * (kc >> 1);
-      const int p_lo = blk + ((kc & 1) ? 4 : 0);
-      const int p_hi = blk + ((kc & 1) ? 12 : 8);
-      bf16_t* row = &Vs[buf][e * ATT_BK];
-      *(u32x2*)(row + att_swz(e, p_lo >> 3) * 8 + (p_lo & 7)) = u32x2{rv[i][0], rv[i][1]};
-      *(u32x2*)(row + att_swz(e, p_hi >> 3) * 8 + (p_hi & 7)) = u32x2{rv[i][2], rv[i][3]};
+      *(u32x4*)(&Vs[buf][e * ATT_BK + att_swz(e, kc) * 8]) = rv[i];
     }
   };
 
@@ -217,31 +222,34 @@ __global__ __launch_bounds__(64 * NW) void attention_bf16_kernel(const bf16_t* _
         s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[st], s[sub], 0, 0, 0);
       }
     }
-    // lane holds keys 32 sub + 8 (v >> 2) + 4 hh + (v & 3) of query qi
+    // lane holds keys 32 sub + 16 (v >> 3) + 8 hh + (v & 7) of query qi
     if (MASKED) {
       const int lo = RANGED ? k_lo : 0, hi = RANGED ? k_hi : len;
       // per-key masking only where the tile crosses some query's range edge
       if (!__all(k0 >= lo && k0 + ATT_BK <= hi)) {
-        const int first = k0 + 4 * hh;
+        const int first = k0 + 8 * hh;
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
-            const int key = first + 32 * sub + 8 * (v >> 2) + (v & 3);
+            const int key = first + 32 * sub + 16 * (v >> 3) + (v & 7);
             if (key < lo || key >= hi) s[sub][v] = -INFINITY;
           }
       }
     }
+    // this lane's maximum; the row's is the larger of it and its partner's
+    // (lane ^ 32), needed only when the reference moves
     float mx = s[0][0];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
       for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[sub][v]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));                  // the row's tile maximum, relative to m_run
     // Move the reference when some row outgrew it by more than the slack, or
-    // sees its first key (a uniform branch, rarely taken after the first tile).
+    // sees its first key (a uniform branch, rarely taken after the first tile;
+    // some row passes the test exactly when some lane's own maximum does).
     const bool fresh = MAYBE_FRESH && m_run == -INFINITY;
     if (__any(fresh ? mx > -INFINITY : mx > slack)) {
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));                // the row's tile maximum, relative to m_run
       const float shift = fresh ? (mx == -INFINITY ? 0.0f : mx) : fmaxf(mx, 0.0f);
       const float alpha = fresh ? 1.0f : __builtin_amdgcn_exp2f(-shift);
       if (!(fresh && mx == -INFINITY)) m_run = fresh ? mx : m_run + shift;
