@@ -1,8 +1,9 @@
 // Row addressing and fused epilogues shared by the GEMM kernels.
 //
-// Every linear map of the tower is a GEMM C = A W^T (A [M, K], W [N, K]) whose
-// epilogue adds the bias and does the step that follows it, so that no
-// separate elementwise pass touches HBM:
+// Every linear map of the tower is a GEMM C = A W^T + b (A [M, K], W [N, K])
+// whose epilogue does the step that follows it, so that no separate
+// elementwise pass touches HBM (the bf16 GEMMs start their accumulators at b;
+// the fp32 GEMM adds b in its epilogue):
 //   conv1     : GELU                               -> bf16 channels-last frames
 //   conv2     : GELU, + sinusoidal position        -> fp32 residual rows
 //   QKV       : + bias; Q, K row-major, V stored transposed per head
@@ -129,9 +130,9 @@ struct Epilogue {
   }
 
   // One 32-row slab of a wave's fp32 tile staged in LDS (row stride LDW floats,
-  // WN columns starting at col0, rows starting at row0), written to C four
-  // consecutive columns per lane: 8- or 16-byte accesses, whole rows
-  // contiguous across lanes. N must be a multiple of 4.
+  // WN columns starting at col0, rows starting at row0; the sums already hold
+  // the bias), written to C four consecutive columns per lane: 8- or 16-byte
+  // accesses, whole rows contiguous across lanes. N must be a multiple of 4.
   template <int WN, int LDW>
   __device__ __forceinline__ static void slab32(const EpiParams& p, const float* slab, int row0, int col0, int lane,
                                                 int M, int N) {
@@ -144,9 +145,8 @@ struct Epilogue {
         const int c = idx >> 3, rq = idx & 7;
         const int n = col0 + c, r0 = row0 + 4 * rq;
         if (n >= N || r0 >= M) continue;
-        const float b = p.bias ? p.bias[n] : 0.0f;
         const float* s = slab + 4 * rq * LDW + c;
-        const float v0 = s[0] + b, v1 = s[LDW] + b, v2 = s[2 * LDW] + b, v3 = s[3 * LDW] + b;
+        const float v0 = s[0], v1 = s[LDW], v2 = s[2 * LDW], v3 = s[3 * LDW];
         bf16_t* dst = p.vt + (int64_t)(n - p.n_split) * p.ld_vt + r0;
         if (r0 + 3 < M) {
           u32x2 w;
@@ -175,10 +175,6 @@ struct Epilogue {
       if (r < M && n < N) {
         o = p.crow.offset(r);
         if (o >= 0) o += n;
-      }
-      if (p.bias && n < N) {
-        const float4 b = *(const float4*)(p.bias + n);
-        v.x += b.x; v.y += b.y; v.z += b.z; v.w += b.w;
       }
       if (EPI == EPI_QKV_BF16 && n < p.q_cols) {
         v.x *= p.q_scale; v.y *= p.q_scale; v.z *= p.q_scale; v.w *= p.q_scale;
