@@ -732,6 +732,9 @@ int forward_impl(aenc_handle* h, const aenc_handle::Ws& w, int B, const void* me
   // under a mask the valid rows (on the device) may be far fewer
   const int M_rows = (int)((int64_t)(B - 1) * T8 + T);
   const bool vary = mask != nullptr;
+  // Without a mask every one of those rows exists: the kernels then take
+  // M_rows as given instead of first reading the row count from the device.
+  const int32_t* const mvr = vary ? mv : nullptr;
 
   if (!q.done(K_MEL, mel_transpose(mel, g.dtype, w.melT, B, C, h->C_pad, F, w.g1, g.dtype, d, s), "mel transpose"))
     return AENC_E_HIP;
@@ -777,7 +780,7 @@ int forward_impl(aenc_handle* h, const aenc_handle::Ws& w, int B, const void* me
   ResidualParts pending{};   // partials the next LayerNorm folds in
   for (int l = 0; l < g.n_layers; ++l) {
     const aenc_handle::Layer& L = h->layers[l];
-    if (!q.done(K_LN, layernorm(w.x, L.ln1_g, L.ln1_b, w.a, g.dtype, M_rows, mv, d, g.ln_eps, s, pending), "ln1"))
+    if (!q.done(K_LN, layernorm(w.x, L.ln1_g, L.ln1_b, w.a, g.dtype, M_rows, mvr, d, g.ln_eps, s, pending), "ln1"))
       return AENC_E_HIP;
     pending = ResidualParts{};
     EpiParams eq{};
@@ -790,11 +793,11 @@ int forward_impl(aenc_handle* h, const aenc_handle::Ws& w, int B, const void* me
       eq.ld_vt = w.ld_vt;
       eq.q_cols = d;                 // the attention kernel takes Q in base-2 score units
       eq.q_scale = ATT_Q_SCALE;
-      e = gemm_bf16(EPI_QKV_BF16, (const bf16_t*)w.a, dense_d, (const bf16_t*)L.qkv_w, d, M_rows, 3 * d, d, mv, eq,
+      e = gemm_bf16(EPI_QKV_BF16, (const bf16_t*)w.a, dense_d, (const bf16_t*)L.qkv_w, d, M_rows, 3 * d, d, mvr, eq,
                     pick_tile(M_rows, 3 * d), s, vary);
     } else {
       eq.crow = dense_rows(3 * d);
-      e = gemm_f32(EPI_STORE_F32, (const float*)w.a, dense_d, (const float*)L.qkv_w, d, M_rows, 3 * d, d, mv, eq, s);
+      e = gemm_f32(EPI_STORE_F32, (const float*)w.a, dense_d, (const float*)L.qkv_w, d, M_rows, 3 * d, d, mvr, eq, s);
     }
     if (!q.done(K_QKV, e, "qkv")) return AENC_E_HIP;
 
@@ -806,7 +809,7 @@ int forward_impl(aenc_handle* h, const aenc_handle::Ws& w, int B, const void* me
     if (!q.done(K_ATTN, e, "attention")) return AENC_E_HIP;
 
     if (split_o > 1) {
-      e = gemm_bf16_splitk((const bf16_t*)w.a, dense_d, (const bf16_t*)L.o_w, d, M_rows, d, d, split_o, mv, w.parts,
+      e = gemm_bf16_splitk((const bf16_t*)w.a, dense_d, (const bf16_t*)L.o_w, d, M_rows, d, d, split_o, mvr, w.parts,
                            d, part_stride, s);
       pending = ResidualParts{w.parts, split_o, part_stride, L.o_b};
     } else {
@@ -814,13 +817,13 @@ int forward_impl(aenc_handle* h, const aenc_handle::Ws& w, int B, const void* me
       eo.bias = L.o_b;
       eo.c = w.x;
       eo.crow = dense_d;
-      e = bf ? gemm_bf16(EPI_RESID_F32, (const bf16_t*)w.a, dense_d, (const bf16_t*)L.o_w, d, M_rows, d, d, mv, eo,
+      e = bf ? gemm_bf16(EPI_RESID_F32, (const bf16_t*)w.a, dense_d, (const bf16_t*)L.o_w, d, M_rows, d, d, mvr, eo,
                          pick_tile(M_rows, d), s, vary)
-             : gemm_f32(EPI_RESID_F32, (const float*)w.a, dense_d, (const float*)L.o_w, d, M_rows, d, d, mv, eo, s);
+             : gemm_f32(EPI_RESID_F32, (const float*)w.a, dense_d, (const float*)L.o_w, d, M_rows, d, d, mvr, eo, s);
     }
     if (!q.done(K_OPROJ, e, "o_proj")) return AENC_E_HIP;
 
-    if (!q.done(K_LN, layernorm(w.x, L.ln2_g, L.ln2_b, w.a, g.dtype, M_rows, mv, d, g.ln_eps, s, pending), "ln2"))
+    if (!q.done(K_LN, layernorm(w.x, L.ln2_g, L.ln2_b, w.a, g.dtype, M_rows, mvr, d, g.ln_eps, s, pending), "ln2"))
       return AENC_E_HIP;
     pending = ResidualParts{};
 
@@ -828,14 +831,14 @@ int forward_impl(aenc_handle* h, const aenc_handle::Ws& w, int B, const void* me
     ef1.bias = L.fc1_b;
     ef1.c = w.hmid;
     ef1.crow = dense_rows(f);
-    e = bf ? gemm_bf16(EPI_GELU_BF16, (const bf16_t*)w.a, dense_d, (const bf16_t*)L.fc1_w, d, M_rows, f, d, mv, ef1,
+    e = bf ? gemm_bf16(EPI_GELU_BF16, (const bf16_t*)w.a, dense_d, (const bf16_t*)L.fc1_w, d, M_rows, f, d, mvr, ef1,
                        pick_tile(M_rows, f), s, vary)
-           : gemm_f32(EPI_GELU_F32, (const float*)w.a, dense_d, (const float*)L.fc1_w, d, M_rows, f, d, mv, ef1, s);
+           : gemm_f32(EPI_GELU_F32, (const float*)w.a, dense_d, (const float*)L.fc1_w, d, M_rows, f, d, mvr, ef1, s);
     if (!q.done(K_FC1, e, "fc1")) return AENC_E_HIP;
 
     if (split_f > 1) {
       e = gemm_bf16_splitk((const bf16_t*)w.hmid, dense_rows(f), (const bf16_t*)L.fc2_w, f, M_rows, d, f, split_f,
-                           mv, w.parts, d, part_stride, s);
+                           mvr, w.parts, d, part_stride, s);
       pending = ResidualParts{w.parts, split_f, part_stride, L.fc2_b};
     } else {
       EpiParams ef2{};
@@ -843,9 +846,9 @@ int forward_impl(aenc_handle* h, const aenc_handle::Ws& w, int B, const void* me
       ef2.c = w.x;
       ef2.crow = dense_d;
       e = bf ? gemm_bf16(EPI_RESID_F32, (const bf16_t*)w.hmid, dense_rows(f), (const bf16_t*)L.fc2_w, f, M_rows, d,
-                         f, mv, ef2, pick_tile(M_rows, d), s, vary)
+                         f, mvr, ef2, pick_tile(M_rows, d), s, vary)
              : gemm_f32(EPI_RESID_F32, (const float*)w.hmid, dense_rows(f), (const float*)L.fc2_w, f, M_rows, d, f,
-                        mv, ef2, s);
+                        mvr, ef2, s);
     }
     if (!q.done(K_FC2, e, "fc2")) return AENC_E_HIP;
   }
@@ -858,7 +861,7 @@ int forward_impl(aenc_handle* h, const aenc_handle::Ws& w, int B, const void* me
   }
 
   const int ph = g.proj_hidden, po = g.proj_out;
-  if (!q.done(K_FINAL, layernorm(w.x, h->lnf_g, h->lnf_b, w.a, g.dtype, M_rows, mv, d, g.ln_eps, s, pending),
+  if (!q.done(K_FINAL, layernorm(w.x, h->lnf_g, h->lnf_b, w.a, g.dtype, M_rows, mvr, d, g.ln_eps, s, pending),
               "final ln"))
     return AENC_E_HIP;
   // Projector rows: the packed LN rows themselves, or (stack k) runs of k
