@@ -1,7 +1,10 @@
 // Calibration kernels: the ceilings the encoder's kernels are measured against
 // on the part itself, beside the published peaks.
-//   * a streaming copy (16-byte vectors, four in flight per lane): the HBM
-//     read+write rate a plain bandwidth-bound kernel reaches;
+//   * a streaming copy (16-byte vectors, four in flight per lane, loads and
+//     stores marked non-temporal, 16384 workgroups): the HBM read+write rate a
+//     bandwidth-bound kernel reaches (the fastest of the copy forms measured:
+//     plain loads and stores 5.76 TB/s, non-temporal 6.06; 8 or 16 vectors in
+//     flight per lane slower);
 //   * a matrix-core loop: chains of v_mfma_f32_32x32x16_bf16 on register
 //     operands (no memory traffic), the bf16 MFMA rate the part sustains. The
 //     operands are non-zero bf16 values whose mantissa bits change every
@@ -20,12 +23,12 @@ __global__ __launch_bounds__(256) void copy4_kernel(u32x4* __restrict__ dst, con
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int64_t i = base + 256 * u;
-      v[u] = i < n16 ? src[i] : u32x4{0u, 0u, 0u, 0u};
+      v[u] = i < n16 ? __builtin_nontemporal_load(src + i) : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int64_t i = base + 256 * u;
-      if (i < n16) dst[i] = v[u];
+      if (i < n16) __builtin_nontemporal_store(v[u], dst + i);
     }
   }
 }
@@ -33,7 +36,7 @@ __global__ __launch_bounds__(256) void copy4_kernel(u32x4* __restrict__ dst, con
 hipError_t copy_stream(void* dst, const void* src, int64_t bytes, hipStream_t stream) {
   if (bytes <= 0 || bytes % 16 != 0) return hipErrorInvalidValue;
   const int64_t n16 = bytes / 16;
-  const int64_t blocks = std::min<int64_t>((n16 + 1023) / 1024, 8192);
+  const int64_t blocks = std::min<int64_t>((n16 + 1023) / 1024, 16384);
   hipLaunchKernelGGL(copy4_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (u32x4*)dst, (const u32x4*)src, n16);
   return hipGetLastError();
 }
