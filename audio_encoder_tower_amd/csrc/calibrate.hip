@@ -5,6 +5,8 @@
 //     bandwidth-bound kernel reaches (the fastest of the copy forms measured:
 //     plain loads and stores 5.76 TB/s, non-temporal 6.06; 8 or 16 vectors in
 //     flight per lane slower);
+//   * LayerNorm's memory traffic without its arithmetic (fp32 rows in, bf16
+//     rows out, the same access pattern): the rate that kernel could reach;
 //   * a matrix-core loop: chains of v_mfma_f32_32x32x16_bf16 on register
 //     operands (no memory traffic), the bf16 MFMA rate the part sustains. The
 //     operands are non-zero bf16 values whose mantissa bits change every
@@ -38,6 +40,37 @@ hipError_t copy_stream(void* dst, const void* src, int64_t bytes, hipStream_t st
   const int64_t n16 = bytes / 16;
   const int64_t blocks = std::min<int64_t>((n16 + 1023) / 1024, 16384);
   hipLaunchKernelGGL(copy4_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (u32x4*)dst, (const u32x4*)src, n16);
+  return hipGetLastError();
+}
+
+// LayerNorm's memory traffic without its arithmetic: one wave per row of d
+// fp32 values, four rows per workgroup, the row read with non-temporal 16-byte
+// loads and written back as bf16 (8 bytes per lane), as the LayerNorm does, but
+// with no reductions between the loads and the stores.
+__global__ __launch_bounds__(256) void row_stream_kernel(const float* __restrict__ x, bf16_t* __restrict__ y,
+                                                         int rows, int d) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int lane = threadIdx.x & 63, n4 = d >> 2;
+  const f32x4* xr = (const f32x4*)(x + (int64_t)row * d);
+  u32x2* yr = (u32x2*)(y + (int64_t)row * d);
+  f32x4 v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    if (lane + 64 * i < n4) v[i] = __builtin_nontemporal_load(xr + lane + 64 * i);
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    if (lane + 64 * i < n4) {
+      u32x2 w;
+      w.x = pack_bf16x2(v[i].x, v[i].y);
+      w.y = pack_bf16x2(v[i].z, v[i].w);
+      yr[lane + 64 * i] = w;
+    }
+}
+
+hipError_t row_stream(const float* x, bf16_t* y, int rows, int d, hipStream_t stream) {
+  if (rows < 1 || d < 4 || d > 2048 || d % 4 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(row_stream_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, x, y, rows, d);
   return hipGetLastError();
 }
 

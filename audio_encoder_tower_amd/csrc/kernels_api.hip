@@ -130,6 +130,12 @@ extern "C" int aenc_k_copy_stream(void* dst, const void* src, int64_t bytes, voi
   return hip_status(copy_stream(dst, src, bytes, (hipStream_t)stream), "copy_stream");
 }
 
+extern "C" int aenc_k_row_stream(const float* x, void* y, int rows, int d, void* stream) {
+  if (!x || !y || rows < 1 || d < 4 || d > 2048 || d % 4) return fail("row stream: need x, y, rows >= 1, d in [4, 2048], d % 4 == 0");
+  if (!aligned16(x) || ((uintptr_t)y & 7)) return fail("row stream: x must be 16-byte and y 8-byte aligned");
+  return hip_status(row_stream(x, (bf16_t*)y, rows, d, (hipStream_t)stream), "row_stream");
+}
+
 extern "C" int aenc_k_mfma_loop(float* out, int blocks, int iters, void* stream) {
   if (!out || blocks < 1 || iters < 1) return fail("mfma loop: need out, blocks >= 1 and iters >= 1");
   return hip_status(mfma_loop(out, blocks, iters, (hipStream_t)stream), "mfma_loop");

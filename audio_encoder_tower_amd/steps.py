@@ -122,6 +122,12 @@ def copy_stream(dst: torch.Tensor, src: torch.Tensor) -> None:
     check(lib().aenc_k_copy_stream(_p(dst), _p(src), nbytes, _s()), "aenc_k_copy_stream")
 
 
+def row_stream(x: torch.Tensor, y: torch.Tensor) -> None:
+    """LayerNorm's traffic without its arithmetic (aenc_k_row_stream): y = bf16(x) row by row."""
+    assert x.dtype == torch.float32 and y.dtype == torch.bfloat16 and x.dim() == 2 and y.shape == x.shape
+    check(lib().aenc_k_row_stream(_p(x), _p(y), x.shape[0], x.shape[1], _s()), "aenc_k_row_stream")
+
+
 def mfma_loop(out: torch.Tensor, blocks: int, iters: int) -> float:
     """The matrix-core loop of the MFMA ceiling (aenc_k_mfma_loop); returns its FLOPs."""
     assert out.dtype == torch.float32 and out.numel() >= blocks * 256

@@ -202,6 +202,13 @@ def ceilings_leg(reps: int = 10):
     ms_plain = timed(lambda: aenc.steps.copy(dst, src), reps)
     assert torch.equal(dst, src)
     del src, dst
+    # LayerNorm's traffic without its arithmetic, on the batch-16 Whisper-large rows
+    rows, d = 24064, 1280
+    x = torch.randn(rows, d, device="cuda")
+    y = torch.empty(rows, d, device="cuda", dtype=torch.bfloat16)
+    ms_rows = timed(lambda: aenc.steps.row_stream(x, y), reps)
+    assert torch.equal(y, x.to(torch.bfloat16))
+    del x, y
     blocks, iters = 4096, 2048
     out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
     flops = blocks * 4.0 * iters * 4 * 32768
@@ -212,6 +219,8 @@ def ceilings_leg(reps: int = 10):
         "copy_frac_of_8tbs": round(2 * nbytes / (ms_copy * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "copy_plain_gbs": round(2 * nbytes / (ms_plain * 1e-3) / 1e9, 1),
         "copy_bytes": 2 * nbytes,
+        "row_stream_gbs": round(rows * d * 6 / (ms_rows * 1e-3) / 1e9, 1),
+        "row_stream": f"{rows} rows of {d} fp32 in, bf16 out: the LayerNorm's accesses without its arithmetic",
         "mfma_bf16_tflops": round(flops / (ms_mfma * 1e-3) / 1e12, 1),
         "mfma_frac_of_peak": round(flops / (ms_mfma * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"], 4),
         "mfma_loop": f"{blocks} workgroups x 4 waves x {iters} rounds x 4 chains of 32x32x16 bf16 MFMAs",
@@ -603,6 +612,7 @@ def main():
         result["mfma_frac_of_measured_ceiling"] = round(tflops / c["mfma_bf16_tflops"], 4)
         if "layernorm" in per_kind:
             per_kind["layernorm"]["frac_of_copy_ceiling"] = round(per_kind["layernorm"]["gbs"] / c["copy_gbs"], 4)
+            per_kind["layernorm"]["frac_of_row_stream"] = round(per_kind["layernorm"]["gbs"] / c["row_stream_gbs"], 4)
         print(f"ceilings: {c}", file=sys.stderr, flush=True)
     if not args.no_configs:
         result["configs"] = configs_leg([n for n in CONFIG_LEGS if n != w.name], args.steps, args.warmup,

@@ -115,6 +115,14 @@ int aenc_k_copy(void *dst, const void *src, int64_t bytes, void *stream);
 int aenc_k_copy_stream(void *dst, const void *src, int64_t bytes, void *stream);
 int aenc_k_mfma_loop(float *out, int blocks, int iters, void *stream);
 
+/* LayerNorm's memory traffic without its arithmetic, the ceiling that kernel
+ * is reported against (not a step of the encoder): y[r][j] = bf16(x[r][j])
+ * (round to nearest even) for `rows` rows of `d` fp32 values (d a multiple
+ * of 4, 4 <= d <= 2048), x row-major and 16-byte aligned, y row-major bf16
+ * and 8-byte aligned, both device memory owned by the caller. One wave per
+ * row, four rows per workgroup, non-temporal row loads, as the LayerNorm. */
+int aenc_k_row_stream(const float *x, void *y, int rows, int d, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

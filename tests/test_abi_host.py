@@ -161,6 +161,10 @@ def test_null_arguments(aenc):
     assert L.aenc_k_copy_stream(None, None, 16, None) == -1
     assert L.aenc_k_mfma_loop(None, 1, 1, None) == -1
     assert L.aenc_k_mfma_loop(ctypes.c_void_p(16), 0, 1, None) == -1
+    assert L.aenc_k_row_stream(None, None, 1, 1280, None) == -1
+    assert L.aenc_k_row_stream(ctypes.c_void_p(16), ctypes.c_void_p(16), 1, 1282, None) == -1
+    assert L.aenc_k_row_stream(ctypes.c_void_p(16), ctypes.c_void_p(16), 0, 1280, None) == -1
+    assert L.aenc_k_row_stream(ctypes.c_void_p(8), ctypes.c_void_p(16), 1, 1280, None) == -1
     # kernel entry points reject bad sizes before any launch
     buf = ctypes.c_void_p(16)
     assert L.aenc_k_gemm_bf16(0, buf, 64, buf, None, buf, 64, 64, 64, 100, -1, None) == -1

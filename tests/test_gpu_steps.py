@@ -147,6 +147,18 @@ def test_layernorm(_lib, d, out):
         np.testing.assert_allclose(host(y), ref, rtol=2 ** -8, atol=1e-6)
 
 
+@pytest.mark.parametrize("rows,d", [(1003, 1280), (37, 1284), (5, 4)])
+def test_row_stream(_lib, rows, d):
+    """The LayerNorm-traffic calibration kernel writes bf16(x), round to
+    nearest even, for every element (its timing is the LayerNorm's ceiling)."""
+    x = torch.randn(rows, d, device=DEV) * 3
+    x[0, :4] = torch.tensor([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -0.0, 65504.0], device=DEV)   # ties, sign
+    y = torch.empty(rows, d, device=DEV, dtype=torch.bfloat16)
+    _lib.steps.row_stream(x, y)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), x.to(torch.bfloat16).view(torch.int16))
+
+
 def packing_contract(mask):
     """The packing the library promises: valid positions in order, each clip
     starting on a multiple of 8 rows."""
