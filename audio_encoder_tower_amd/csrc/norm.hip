@@ -52,15 +52,28 @@ __device__ __forceinline__ float4 add4(float4 a, float4 b) {
 }
 
 // The residual update of a split product: v (row `row` of x) += bias + every
-// partial row, in that order.
+// partial row, in that order. All parts' loads are issued before the first
+// add (a loop over a run-time part count would wait for each part in turn).
+constexpr int LN_MAX_PARTS = 4;
 __device__ __forceinline__ void fold_parts(float4 (&v)[LN_MAXV], const ResidualParts& rp, int64_t row, int d,
                                            int n4, int lane) {
+  float4 q[LN_MAX_PARTS][LN_MAXV];
+#pragma unroll
+  for (int s = 0; s < LN_MAX_PARTS; ++s)
+    if (s < rp.n) {
+      const float4* src = (const float4*)(rp.parts + s * rp.stride + row * d);
+#pragma unroll
+      for (int i = 0; i < LN_MAXV; ++i)
+        if (lane + 64 * i < n4) q[s][i] = src[lane + 64 * i];
+    }
 #pragma unroll
   for (int i = 0; i < LN_MAXV; ++i) {
     const int j = lane + 64 * i;
     if (j >= n4) continue;
     float4 p = rp.bias ? ((const float4*)rp.bias)[j] : make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s = 0; s < rp.n; ++s) p = add4(p, ((const float4*)(rp.parts + s * rp.stride + row * d))[j]);
+#pragma unroll
+    for (int s = 0; s < LN_MAX_PARTS; ++s)
+      if (s < rp.n) p = add4(p, q[s][i]);
     v[i] = add4(v[i], p);
   }
 }
@@ -108,7 +121,8 @@ __global__ __launch_bounds__(256) void layernorm_kernel(float* __restrict__ x, c
 
 hipError_t layernorm(float* x, const float* gamma, const float* beta, void* y, int y_dtype, int M,
                      const int32_t* m_dev, int d, float eps, hipStream_t stream, ResidualParts rp) {
-  if (d % 4 != 0 || d > 64 * 4 * LN_MAXV || M <= 0 || (rp.n > 0 && !rp.parts)) return hipErrorInvalidValue;
+  if (d % 4 != 0 || d > 64 * 4 * LN_MAXV || M <= 0 || (rp.n > 0 && !rp.parts) || rp.n > LN_MAX_PARTS)
+    return hipErrorInvalidValue;
   dim3 grid((M + 3) / 4);
   if (y_dtype == 1 && rp.n > 0)
     hipLaunchKernelGGL((layernorm_kernel<bf16_t, true>), grid, dim3(256), 0, stream, x, gamma, beta, (bf16_t*)y, M,
@@ -177,7 +191,8 @@ __global__ __launch_bounds__(256) void final_ln_kernel(const float* __restrict__
 hipError_t final_ln_out(const float* x, const int32_t* map, const float* gamma, const float* beta, void* out,
                         int out_dtype, int B, int T, int pool, int d, float eps, hipStream_t stream,
                         ResidualParts rp) {
-  if (d % 4 != 0 || d > 64 * 4 * LN_MAXV || (pool != 1 && pool != 2) || (rp.n > 0 && !rp.parts))
+  if (d % 4 != 0 || d > 64 * 4 * LN_MAXV || (pool != 1 && pool != 2) || (rp.n > 0 && !rp.parts) ||
+      rp.n > LN_MAX_PARTS)
     return hipErrorInvalidValue;
   const int rows = B * (T / pool);
   if (rows <= 0) return hipSuccess;
