@@ -83,7 +83,7 @@ SIGNATURES = {
                                 c_void_p]),
     "aenc_k_copy": (c_int, [c_void_p, c_void_p, c_int64, c_void_p]),
     "aenc_k_copy_stream": (c_int, [c_void_p, c_void_p, c_int64, c_void_p]),
-    "aenc_k_mfma_loop": (c_int, [c_void_p, c_int, c_int, c_void_p]),
+    "aenc_k_mfma_loop": (c_int, [c_void_p, c_int, c_int, c_void_p, c_void_p]),
     "aenc_k_row_stream": (c_int, [c_void_p, c_void_p, c_int, c_int, c_void_p]),
     "aenc_handle_geometry": (c_int, [c_void_p, POINTER(Geometry)]),
     "aenc_forward_noalloc": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_void_p]),

@@ -12,6 +12,10 @@
 //     operands are non-zero bf16 values whose mantissa bits change every
 //     iteration, since the matrix cores draw less power, and clock higher, on
 //     zeros or constant inputs than on the varied data of a real product.
+//     Optionally each workgroup's first wave also counts the shader clock
+//     (s_memtime) and the 100 MHz real-time counter (s_memrealtime) around its
+//     loop, which gives the clock the loop ran at: the part lowers its clock
+//     under a sustained matrix-core load.
 #include "common.h"
 #include "launch.h"
 
@@ -77,8 +81,11 @@ hipError_t row_stream(const float* x, bf16_t* y, int rows, int d, hipStream_t st
 constexpr int MFMA_CHAINS = 4;
 
 // Each wave runs `iters` rounds of MFMA_CHAINS independent 32x32x16 MFMAs and
-// writes one sum per lane to out[global thread id].
-__global__ __launch_bounds__(256) void mfma_loop_kernel(float* __restrict__ out, int iters) {
+// writes one sum per lane to out[global thread id]; with ticks, wave 0 of
+// workgroup b writes the shader-clock and real-time ticks its loop took to
+// ticks[2 b] and ticks[2 b + 1].
+__global__ __launch_bounds__(256) void mfma_loop_kernel(float* __restrict__ out, uint64_t* __restrict__ ticks,
+                                                        int iters) {
   const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // bf16 pairs with exponent 126..127 (values in [0.5, 2)) and lane-dependent
   // signs and mantissas
@@ -94,6 +101,11 @@ __global__ __launch_bounds__(256) void mfma_loop_kernel(float* __restrict__ out,
   for (int c = 0; c < MFMA_CHAINS; ++c)
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[c][v] = 0.0f;
+  uint64_t t0 = 0, r0 = 0;
+  if (ticks && wave == 0) {
+    t0 = __builtin_amdgcn_s_memtime();
+    r0 = __builtin_amdgcn_s_memrealtime();
+  }
   for (int it = 0; it < iters; ++it) {
     const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{sa[0], sa[1], sa[2], sa[3]});
     const bf16x8 b = __builtin_bit_cast(bf16x8, u32x4{sb[0], sb[1], sb[2], sb[3]});
@@ -112,11 +124,19 @@ __global__ __launch_bounds__(256) void mfma_loop_kernel(float* __restrict__ out,
 #pragma unroll
     for (int v = 0; v < 16; ++v) s += acc[c][v];
   out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
+  if (ticks && wave == 0) {
+    // the accumulators are final here: the sum above waited for the last MFMAs
+    const uint64_t t1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+    if (lane == 0) {
+      ticks[2 * (int64_t)blockIdx.x] = t1 - t0;
+      ticks[2 * (int64_t)blockIdx.x + 1] = r1 - r0;
+    }
+  }
 }
 
-hipError_t mfma_loop(float* out, int blocks, int iters, hipStream_t stream) {
+hipError_t mfma_loop(float* out, uint64_t* ticks, int blocks, int iters, hipStream_t stream) {
   if (blocks < 1 || iters < 1) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(mfma_loop_kernel, dim3(blocks), dim3(256), 0, stream, out, iters);
+  hipLaunchKernelGGL(mfma_loop_kernel, dim3(blocks), dim3(256), 0, stream, out, ticks, iters);
   return hipGetLastError();
 }
 

@@ -136,7 +136,8 @@ extern "C" int aenc_k_row_stream(const float* x, void* y, int rows, int d, void*
   return hip_status(row_stream(x, (bf16_t*)y, rows, d, (hipStream_t)stream), "row_stream");
 }
 
-extern "C" int aenc_k_mfma_loop(float* out, int blocks, int iters, void* stream) {
+extern "C" int aenc_k_mfma_loop(float* out, int blocks, int iters, uint64_t* ticks, void* stream) {
   if (!out || blocks < 1 || iters < 1) return fail("mfma loop: need out, blocks >= 1 and iters >= 1");
-  return hip_status(mfma_loop(out, blocks, iters, (hipStream_t)stream), "mfma_loop");
+  if ((uintptr_t)ticks & 7) return fail("mfma loop: ticks must be 8-byte aligned");
+  return hip_status(mfma_loop(out, ticks, blocks, iters, (hipStream_t)stream), "mfma_loop");
 }

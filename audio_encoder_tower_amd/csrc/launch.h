@@ -130,7 +130,7 @@ hipError_t copy_bytes(void* dst, const void* src, int64_t bytes, hipStream_t str
 // workgroups of 4 waves, each wave `iters` rounds of 4 independent
 // 32x32x16 bf16 MFMAs (the matrix-core ceiling); out holds blocks * 256 floats.
 hipError_t copy_stream(void* dst, const void* src, int64_t bytes, hipStream_t stream);
-hipError_t mfma_loop(float* out, int blocks, int iters, hipStream_t stream);
+hipError_t mfma_loop(float* out, uint64_t* ticks, int blocks, int iters, hipStream_t stream);
 hipError_t row_stream(const float* x, bf16_t* y, int rows, int d, hipStream_t stream);
 
 }  // namespace aenc

@@ -128,8 +128,12 @@ def row_stream(x: torch.Tensor, y: torch.Tensor) -> None:
     check(lib().aenc_k_row_stream(_p(x), _p(y), x.shape[0], x.shape[1], _s()), "aenc_k_row_stream")
 
 
-def mfma_loop(out: torch.Tensor, blocks: int, iters: int) -> float:
-    """The matrix-core loop of the MFMA ceiling (aenc_k_mfma_loop); returns its FLOPs."""
+def mfma_loop(out: torch.Tensor, blocks: int, iters: int, ticks: torch.Tensor = None) -> float:
+    """The matrix-core loop of the MFMA ceiling (aenc_k_mfma_loop); returns its FLOPs.
+    ticks: None or int64 [blocks, 2] for each workgroup's shader-clock and
+    100 MHz real-time ticks around its loop."""
     assert out.dtype == torch.float32 and out.numel() >= blocks * 256
-    check(lib().aenc_k_mfma_loop(_p(out), blocks, iters, _s()), "aenc_k_mfma_loop")
+    if ticks is not None:
+        assert ticks.dtype == torch.int64 and ticks.is_contiguous() and ticks.numel() >= 2 * blocks
+    check(lib().aenc_k_mfma_loop(_p(out), blocks, iters, _p(ticks), _s()), "aenc_k_mfma_loop")
     return float(blocks) * 4 * iters * 4 * 32768

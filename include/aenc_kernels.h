@@ -111,9 +111,13 @@ int aenc_k_copy(void *dst, const void *src, int64_t bytes, void *stream);
  * rounds of 4 independent v_mfma_f32_32x32x16_bf16 (32768 FLOP each) on
  * register operands with varied non-zero bf16 values, and writes one sum per
  * lane to out (fp32, blocks * 256 elements): the bf16 matrix-core rate with
- * no memory traffic. FLOPs per launch = blocks * 4 * iters * 4 * 32768. */
+ * no memory traffic. FLOPs per launch = blocks * 4 * iters * 4 * 32768.
+ * ticks: NULL, or uint64 [2 * blocks] (8-byte aligned) that receives, per
+ * workgroup, the shader-clock cycles (s_memtime) and the 100 MHz real-time
+ * ticks (s_memrealtime) its first wave counted around its loop; 1e8 times
+ * their ratio is the shader clock in Hz that the loop ran at. */
 int aenc_k_copy_stream(void *dst, const void *src, int64_t bytes, void *stream);
-int aenc_k_mfma_loop(float *out, int blocks, int iters, void *stream);
+int aenc_k_mfma_loop(float *out, int blocks, int iters, uint64_t *ticks, void *stream);
 
 /* LayerNorm's memory traffic without its arithmetic, the ceiling that kernel
  * is reported against (not a step of the encoder): y[r][j] = bf16(x[r][j])

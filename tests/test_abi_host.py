@@ -159,8 +159,9 @@ def test_null_arguments(aenc):
     assert L.aenc_k_gemm_bf16(0, None, 0, None, None, None, 0, 1, 1, 64, -1, None) == -1
     assert L.aenc_k_copy(None, None, 16, None) == -1
     assert L.aenc_k_copy_stream(None, None, 16, None) == -1
-    assert L.aenc_k_mfma_loop(None, 1, 1, None) == -1
-    assert L.aenc_k_mfma_loop(ctypes.c_void_p(16), 0, 1, None) == -1
+    assert L.aenc_k_mfma_loop(None, 1, 1, None, None) == -1
+    assert L.aenc_k_mfma_loop(ctypes.c_void_p(16), 0, 1, None, None) == -1
+    assert L.aenc_k_mfma_loop(ctypes.c_void_p(16), 1, 1, ctypes.c_void_p(12), None) == -1
     assert L.aenc_k_row_stream(None, None, 1, 1280, None) == -1
     assert L.aenc_k_row_stream(ctypes.c_void_p(16), ctypes.c_void_p(16), 1, 1282, None) == -1
     assert L.aenc_k_row_stream(ctypes.c_void_p(16), ctypes.c_void_p(16), 0, 1280, None) == -1

@@ -159,6 +159,25 @@ def test_row_stream(_lib, rows, d):
     assert torch.equal(y.view(torch.int16), x.to(torch.bfloat16).view(torch.int16))
 
 
+def test_mfma_loop_clock_ticks(_lib):
+    """The MFMA-ceiling loop's optional tick record: every workgroup reports a
+    positive shader-clock and real-time count, whose ratio gives a clock in
+    the part's range, and the loop's sums are the same with or without it."""
+    blocks, iters = 512, 64
+    a = torch.empty(blocks * 256, device=DEV)
+    b = torch.empty(blocks * 256, device=DEV)
+    ticks = torch.zeros(blocks, 2, dtype=torch.int64, device=DEV)
+    _lib.steps.mfma_loop(a, blocks, iters)
+    _lib.steps.mfma_loop(b, blocks, iters, ticks)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(a).all()) and torch.equal(a, b)
+    t = ticks.cpu()
+    assert bool((t > 0).all()), t[:4]
+    ghz = (t[:, 0].double() / t[:, 1].double()) * 0.1
+    print(f"mfma loop clock: median {float(ghz.median()):.3f} GHz", flush=True)
+    assert 0.3 < float(ghz.median()) < 3.0
+
+
 def packing_contract(mask):
     """The packing the library promises: valid positions in order, each clip
     starting on a multiple of 8 rows."""
