@@ -27,7 +27,11 @@ one's busy cycles, so cycles = GRBM_GUI_ACTIVE / XCDs (8 on MI355X), and the
 clock is cycles over the profiled dispatch time. MFMA busy is
 SQ_VALU_MFMA_BUSY_CYCLES / (cycles x 1024 SIMDs), the fraction of SIMD
 cycles with a matrix instruction in flight (256 CUs x 4 SIMDs), and CU busy
-SQ_BUSY_CU_CYCLES / (cycles x 256).
+SQ_BUSY_CU_CYCLES / (cycles x 256). On MI355X these cycles come out ~1.25
+times the shader-clock cycles that s_memtime counts inside the same kernels
+(and imply clocks above the part's 2.4 GHz for short memory-bound kernels),
+so the derived clock is an overestimate and the busy fractions are
+correspondingly low.
 Measurement tooling only: nothing on the forward path imports it.
 """
 from __future__ import annotations
