@@ -27,11 +27,11 @@ one's busy cycles, so cycles = GRBM_GUI_ACTIVE / XCDs (8 on MI355X), and the
 clock is cycles over the profiled dispatch time. MFMA busy is
 SQ_VALU_MFMA_BUSY_CYCLES / (cycles x 1024 SIMDs), the fraction of SIMD
 cycles with a matrix instruction in flight (256 CUs x 4 SIMDs), and CU busy
-SQ_BUSY_CU_CYCLES / (cycles x 256). On MI355X these cycles come out ~1.25
-times the shader-clock cycles that s_memtime counts inside the same kernels
-(and imply clocks above the part's 2.4 GHz for short memory-bound kernels),
-so the derived clock is an overestimate and the busy fractions are
-correspondingly low.
+SQ_BUSY_CU_CYCLES / (cycles x 256). On MI355X GRBM_GUI_ACTIVE counts over a
+somewhat longer window than the dispatch timestamps: for a 2.45 ms kernel the
+derived clock matches the shader clock that s_memtime counts inside it, for
+the encoder's 0.1-0.3 ms GEMMs it reads 9-20% high, and for 30 us kernels it
+exceeds the part's 2.4 GHz; the busy fractions are low by the same factor.
 Measurement tooling only: nothing on the forward path imports it.
 """
 from __future__ import annotations
